@@ -1,0 +1,64 @@
+"""Build libgro.so (the C-ABI library) in-tree for gfx950.
+
+    python -m gradient_reduction_optimizer_amd.build
+
+The planner is plain C++ (g++); the device entry points and kernels are HIP
+(hipcc, gfx950 only).  No contraction of FP operations anywhere, so each
+FP32 step rounds once; packed-FP32 instruction selection is switched off.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgro.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libgro.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    o = os.path.join(BUILD, "plan.o")
+    _run(["g++", *COMMON, "-c", os.path.join(CSRC, "plan.cpp"), "-o", o], verbose)
+    objs.append(o)
+    for name in ("kernels", "abi"):
+        o = os.path.join(BUILD, f"{name}.o")
+        _run([HIPCC, *COMMON, *HIP_FLAGS, "-c", os.path.join(CSRC, f"{name}.hip"), "-o", o], verbose)
+        objs.append(o)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def device_asm(out_path: str) -> str:
+    """Write the gfx950 assembly of the kernels (for inspection)."""
+    _run([HIPCC, *COMMON, *HIP_FLAGS, "--cuda-device-only", "-S",
+          os.path.join(CSRC, "kernels.hip"), "-o", out_path], False)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

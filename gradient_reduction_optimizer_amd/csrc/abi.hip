@@ -1,0 +1,258 @@
+// C-ABI entry points that touch the device: binding, accumulate, norm,
+// clip + AdamW.  All validation (arguments and the accumulation-window
+// bookkeeping) happens on the host before the first launch, so a call that
+// returns an error has enqueued nothing (Mixle "Distributed Transformer
+// Training", section "Backend split": fail before fitting).
+//
+// Window semantics follow NeMo Automodel issue #3857, "refactor(distributed):
+// establish shared native TP replica ownership", sections "Preserved prototype
+// and evidence" and "Proposed scope and acceptance criteria": accumulation
+// over 1, >1 and trailing (shorter) windows, each divided by the number of
+// microbatches it actually holds; global norms; clipping on or off; Adam(W)
+// updates.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "kernels.h"
+#include "plan.h"
+
+using namespace gro;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return set_error(GRO_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_bound(const gro_plan* p) {
+  if (p == nullptr) return set_error(GRO_E_INVALID, "plan is NULL");
+  if (!p->bound) return set_error(GRO_E_STATE, "plan is not bound to a workspace");
+  return GRO_OK;
+}
+
+const ChunkDev* dev_chunks(const gro_plan* p) {
+  return reinterpret_cast<const ChunkDev*>(p->d_ws + p->ws.chunk_off);
+}
+const BucketDev* dev_buckets(const gro_plan* p) {
+  return reinterpret_cast<const BucketDev*>(p->d_ws + p->ws.bucket_off);
+}
+double* dev_partials(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.partial_off); }
+double* dev_scalars(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.scalar_off); }
+
+void reset_window(gro_plan* p) {
+  std::fill(p->count.begin(), p->count.end(), 0);
+  std::fill(p->partials_ready.begin(), p->partials_ready.end(), 0);
+  p->acc_ptr = nullptr;
+  p->norm_done = false;
+  p->norm_window = 0;
+}
+
+}  // namespace
+
+extern "C" int gro_plan_bind(gro_plan* p, void* d_workspace, uint64_t bytes, void* stream) {
+  clear_error();
+  if (p == nullptr || d_workspace == nullptr) return set_error(GRO_E_INVALID, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(d_workspace) & 255u)
+    return set_error(GRO_E_INVALID, "workspace must be 256-byte aligned");
+  if (bytes < p->ws.total)
+    return set_error(GRO_E_INVALID, "workspace has %llu bytes, plan needs %llu",
+                     (unsigned long long)bytes, (unsigned long long)p->ws.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(d_workspace);
+  hipError_t e = hipSuccess;
+  if (!p->bucket_dev.empty())
+    e = hipMemcpyAsync(ws + p->ws.bucket_off, p->bucket_dev.data(),
+                       p->bucket_dev.size() * sizeof(BucketDev), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && !p->chunks.empty())
+    e = hipMemcpyAsync(ws + p->ws.chunk_off, p->chunks.data(), p->chunks.size() * sizeof(ChunkDev),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "gro_plan_bind upload");
+  int dev = -1;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  p->d_ws = ws;
+  p->bound = true;
+  p->device = dev;
+  reset_window(p);
+  return GRO_OK;
+}
+
+extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
+                              float* d_acc, int32_t micro_index, int32_t window_size, void* stream) {
+  clear_error();
+  int rc = check_bound(p);
+  if (rc != GRO_OK) return rc;
+  const int32_t nb = int32_t(p->buckets.size());
+  if (b0 < 0 || b1 < b0 || b1 > nb)
+    return set_error(GRO_E_INVALID, "bucket range [%d, %d) not within [0, %d)", b0, b1, nb);
+  if (micro_index < 0) return set_error(GRO_E_INVALID, "micro_index < 0");
+  if (window_size < 0) return set_error(GRO_E_INVALID, "window_size < 0");
+  if (window_size > 0 && micro_index >= window_size)
+    return set_error(GRO_E_INVALID, "micro_index %d outside a window of %d", micro_index, window_size);
+  if (b1 == b0) return GRO_OK;
+  if (d_grad_buckets == nullptr) return set_error(GRO_E_INVALID, "d_grad_buckets is NULL");
+  if (d_acc == nullptr || !aligned16(d_acc))
+    return set_error(GRO_E_INVALID, "d_acc must be a non-NULL 16-byte aligned device pointer");
+  for (int32_t b = b0; b < b1; ++b) {
+    const void* g = d_grad_buckets[b - b0];
+    if (g == nullptr || !aligned16(g))
+      return set_error(GRO_E_INVALID, "gradient buffer of bucket %d is NULL or not 16-byte aligned", b);
+    if (micro_index != 0 && p->count[size_t(b)] != micro_index)
+      return set_error(GRO_E_STATE, "bucket %d has accumulated %d microbatches, not %d", b,
+                       p->count[size_t(b)], micro_index);
+  }
+  if (micro_index != 0 && p->acc_ptr != nullptr && p->acc_ptr != d_acc)
+    return set_error(GRO_E_STATE, "a different accumulator than earlier in this window");
+
+  const bool fuse = window_size > 0 && micro_index == window_size - 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t lb = b0; lb < b1; lb += kMaxBucketsPerLaunch) {
+    const int32_t le = (b1 - lb) < kMaxBucketsPerLaunch ? b1 : lb + kMaxBucketsPerLaunch;
+    AccumulateLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.chunks = dev_chunks(p);
+    a.buckets = dev_buckets(p);
+    a.q_begin = p->buckets[size_t(lb)].first_chunk;
+    a.q_end = p->buckets[size_t(le - 1)].first_chunk + p->buckets[size_t(le - 1)].n_chunks;
+    a.b_first = lb;
+    a.n_grads = le - lb;
+    for (int32_t b = lb; b < le; ++b) a.grads[b - lb] = static_cast<const uint16_t*>(d_grad_buckets[b - b0]);
+    a.acc = d_acc;
+    a.partials = dev_partials(p);
+    a.R = p->R;
+    a.micro_index = micro_index;
+    a.fuse_norm = fuse ? 1 : 0;
+    a.window = window_size;
+    const hipError_t e = launch_accumulate(a, s);
+    if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+  }
+  for (int32_t b = b0; b < b1; ++b) {
+    p->count[size_t(b)] = micro_index + 1;
+    p->partials_ready[size_t(b)] = fuse ? 1 : 0;
+  }
+  p->acc_ptr = d_acc;
+  p->norm_done = false;
+  return GRO_OK;
+}
+
+extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_size, void* stream) {
+  clear_error();
+  int rc = check_bound(p);
+  if (rc != GRO_OK) return rc;
+  if (window_size < 1) return set_error(GRO_E_INVALID, "window_size must be >= 1");
+  const int32_t nb = int32_t(p->buckets.size());
+  if (nb > 0 && (d_acc == nullptr || !aligned16(d_acc)))
+    return set_error(GRO_E_INVALID, "d_acc must be a non-NULL 16-byte aligned device pointer");
+  for (int32_t b = 0; b < nb; ++b)
+    if (p->count[size_t(b)] != window_size)
+      return set_error(GRO_E_STATE, "bucket %d has accumulated %d microbatches, window is %d", b,
+                       p->count[size_t(b)], window_size);
+  if (nb > 0 && d_acc != p->acc_ptr)
+    return set_error(GRO_E_STATE, "d_acc is not the accumulator of this window");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Stage 1 for runs of buckets whose partials the last accumulate did not write.
+  int32_t b = 0;
+  while (b < nb) {
+    if (p->partials_ready[size_t(b)]) {
+      ++b;
+      continue;
+    }
+    int32_t e = b;
+    while (e < nb && !p->partials_ready[size_t(e)]) ++e;
+    NormLaunch a;
+    a.chunks = dev_chunks(p);
+    a.acc = d_acc;
+    a.partials = dev_partials(p);
+    a.q_begin = p->buckets[size_t(b)].first_chunk;
+    a.q_end = p->buckets[size_t(e - 1)].first_chunk + p->buckets[size_t(e - 1)].n_chunks;
+    a.window = window_size;
+    const hipError_t err = launch_norm_partials(a, s);
+    if (err != hipSuccess) return hip_fail(err, "norm stage-1 launch");
+    b = e;
+  }
+  const hipError_t err = launch_norm_final(dev_partials(p), int64_t(p->chunks.size()), dev_scalars(p), s);
+  if (err != hipSuccess) return hip_fail(err, "norm stage-2 launch");
+  std::fill(p->partials_ready.begin(), p->partials_ready.end(), 1);
+  p->norm_done = true;
+  p->norm_window = window_size;
+  p->norm_stream = stream;
+  return GRO_OK;
+}
+
+extern "C" int gro_plan_get_norm(gro_plan* p, double* norm, double* norm_sq, int32_t* finite) {
+  clear_error();
+  int rc = check_bound(p);
+  if (rc != GRO_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(p->norm_stream);
+  double host[kNumScalars];
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(host, dev_scalars(p), sizeof(host), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the norm");
+  if (norm) *norm = host[kNorm];
+  if (norm_sq) *norm_sq = host[kNormSq];
+  if (finite) *finite = host[kFinite] != 0.0 ? 1 : 0;
+  return GRO_OK;
+}
+
+extern "C" int gro_clip_adamw(gro_plan* p, const float* d_acc, int32_t window_size, double max_norm,
+                              const gro_adamw_hparams* hp, int64_t step, float* d_master, float* d_m,
+                              float* d_v, uint16_t* d_param_bf16, void* stream) {
+  clear_error();
+  int rc = check_bound(p);
+  if (rc != GRO_OK) return rc;
+  if (hp == nullptr) return set_error(GRO_E_INVALID, "hp is NULL");
+  if (step < 1) return set_error(GRO_E_INVALID, "step must be >= 1");
+  if (window_size < 1) return set_error(GRO_E_INVALID, "window_size must be >= 1");
+  if (std::isnan(max_norm)) return set_error(GRO_E_INVALID, "max_norm is NaN");
+  if (!(hp->lr >= 0.0) || !std::isfinite(hp->lr) || !(hp->eps >= 0.0) || !std::isfinite(hp->eps) ||
+      !(hp->weight_decay >= 0.0) || !std::isfinite(hp->weight_decay) || !(hp->beta1 >= 0.0) ||
+      !(hp->beta1 < 1.0) || !(hp->beta2 >= 0.0) || !(hp->beta2 < 1.0))
+    return set_error(GRO_E_INVALID, "hyper-parameters out of range (lr, eps, wd >= 0; 0 <= beta < 1)");
+  const bool any = !p->buckets.empty();
+  if (any) {
+    if (d_acc == nullptr || !aligned16(d_acc) || d_master == nullptr || !aligned16(d_master) ||
+        d_m == nullptr || !aligned16(d_m) || d_v == nullptr || !aligned16(d_v) ||
+        (d_param_bf16 != nullptr && !aligned16(d_param_bf16)))
+      return set_error(GRO_E_INVALID, "state pointers must be non-NULL and 16-byte aligned");
+    if (d_acc != p->acc_ptr) return set_error(GRO_E_STATE, "d_acc is not the accumulator of this window");
+  }
+  if (!p->norm_done || p->norm_window != window_size)
+    return set_error(GRO_E_STATE, "gro_reduce_norm of this window (size %d) has not run", window_size);
+
+  // Per-step scalars in FP64 from the hyper-parameters as given, each rounded
+  // once to FP32.
+  const double bc1 = 1.0 - std::pow(hp->beta1, double(step));
+  const double bc2 = 1.0 - std::pow(hp->beta2, double(step));
+  AdamWLaunch a;
+  std::memset(&a, 0, sizeof(a));
+  a.chunks = dev_chunks(p);
+  a.buckets = dev_buckets(p);
+  a.n_chunks = int64_t(p->chunks.size());
+  a.acc = d_acc;
+  a.master = d_master;
+  a.m = d_m;
+  a.v = d_v;
+  a.p_bf16 = d_param_bf16;
+  a.scalars = dev_scalars(p);
+  a.max_norm = max_norm;
+  a.clip_on = (max_norm > 0.0 && !std::isinf(max_norm)) ? 1 : 0;
+  a.window = window_size;
+  a.beta1 = float(hp->beta1);
+  a.beta2 = float(hp->beta2);
+  a.one_minus_beta1 = float(1.0 - hp->beta1);
+  a.one_minus_beta2 = float(1.0 - hp->beta2);
+  a.step_size = float(hp->lr / bc1);
+  a.sqrt_bc2 = float(std::sqrt(bc2));
+  a.eps = float(hp->eps);
+  a.decay = float(1.0 - hp->lr * hp->weight_decay);
+  const hipError_t e = launch_adamw(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "clip+AdamW launch");
+  reset_window(p);
+  return GRO_OK;
+}

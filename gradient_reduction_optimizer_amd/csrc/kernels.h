@@ -1,0 +1,61 @@
+// Launchers for the gfx950 kernels (kernels.hip).  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace gro {
+
+// Buckets whose gradient pointers travel in one launch's kernel arguments.
+constexpr int kMaxBucketsPerLaunch = 64;
+
+struct AccumulateLaunch {
+  const ChunkDev* chunks;   // device chunk table
+  const BucketDev* buckets; // device bucket table
+  int64_t q_begin, q_end;   // chunk range [q_begin, q_end)
+  int32_t b_first;          // bucket index of grads[0]
+  int32_t n_grads;
+  const uint16_t* grads[kMaxBucketsPerLaunch];
+  float* acc;
+  double* partials;         // norm partials (written only when fuse_norm)
+  int32_t R;
+  int32_t micro_index;
+  int32_t fuse_norm;
+  int32_t window;           // microbatches in the window (used when fuse_norm)
+};
+
+struct NormLaunch {
+  const ChunkDev* chunks;
+  const float* acc;
+  double* partials;
+  int64_t q_begin, q_end;
+  int32_t window;
+};
+
+struct AdamWLaunch {
+  const ChunkDev* chunks;
+  const BucketDev* buckets;
+  int64_t n_chunks;
+  const float* acc;
+  float* master;
+  float* m;
+  float* v;
+  uint16_t* p_bf16;         // may be null
+  const double* scalars;    // norm written by the norm's second stage
+  double max_norm;
+  int32_t clip_on;
+  int32_t window;
+  float beta1, beta2, one_minus_beta1, one_minus_beta2;
+  float step_size, sqrt_bc2, eps, decay;
+};
+
+hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s);
+hipError_t launch_norm_partials(const NormLaunch& a, hipStream_t s);
+hipError_t launch_norm_final(const double* partials, int64_t n_chunks, double* scalars,
+                             hipStream_t s);
+hipError_t launch_adamw(const AdamWLaunch& a, hipStream_t s);
+
+}  // namespace gro

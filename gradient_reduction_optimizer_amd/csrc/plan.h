@@ -1,0 +1,76 @@
+// Internal host-side plan structures shared by the planner (plan.cpp, plain
+// C++) and the HIP entry points (abi.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+#include <vector>
+
+#include "gro.h"
+
+namespace gro {
+
+// Elements per chunk.  A chunk is one workgroup's unit of work in every pass
+// and the granularity of the global norm's partial sums, so the norm's
+// summation order is fixed by the plan, never by the launch shape.
+constexpr int32_t kChunkElems = 16384;
+// Bucket bases and slot strides are multiples of this many elements
+// (256 B of FP32, 128 B of BF16) so every chunk starts 128-bit aligned.
+constexpr int64_t kAlignElems = 64;
+constexpr int64_t kMaxNumel = int64_t(1) << 46;
+
+// Device-side tables, uploaded by gro_plan_bind.
+struct ChunkDev {          // 16 B
+  int64_t begin;           // flat index of the chunk's first element
+  int32_t len;             // elements, 1..kChunkElems
+  int32_t bucket;
+};
+struct BucketDev {         // 32 B
+  int64_t base;            // flat index of the bucket's first element
+  int64_t stride;          // slot stride of its BF16 gradient buffer
+  int32_t owner;           // GRO_OWNER_*
+  int32_t slots;
+  int32_t decayed;
+  int32_t reserved;
+};
+static_assert(sizeof(ChunkDev) == 16, "chunk table entry is 16 bytes");
+static_assert(sizeof(BucketDev) == 32, "bucket table entry is 32 bytes");
+
+// Device scalars written by the norm's second stage.
+enum ScalarSlot { kNormSq = 0, kNorm = 1, kFinite = 2, kNumScalars = 8 };
+
+struct WorkspaceLayout {
+  uint64_t bucket_off = 0, chunk_off = 0, partial_off = 0, scalar_off = 0, total = 0;
+};
+
+inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+
+}  // namespace gro
+
+struct gro_plan {
+  int32_t R = 0;
+  int64_t bucket_elems = 0;
+  int64_t n_flat = 0;
+  int64_t n_owned = 0;
+  std::vector<gro_tensor_layout> tensors;
+  std::vector<gro_bucket_info> buckets;
+  std::vector<gro::BucketDev> bucket_dev;
+  std::vector<gro::ChunkDev> chunks;
+  gro::WorkspaceLayout ws;
+
+  // Binding.
+  char* d_ws = nullptr;
+  bool bound = false;
+  int device = -1;
+
+  // Window bookkeeping (host side, validated before any launch).
+  std::vector<int32_t> count;          // microbatches accumulated per bucket
+  std::vector<uint8_t> partials_ready; // norm partials written by the last accumulate
+  const float* acc_ptr = nullptr;      // accumulator used in this window
+  bool norm_done = false;
+  int32_t norm_window = 0;
+  void* norm_stream = nullptr;
+};

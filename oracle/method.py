@@ -200,7 +200,7 @@ def clip_coefficient(norm: float, max_norm: float):
     """
     if not math.isfinite(norm):
         return F32(1.0), False
-    mx = float(F32(max_norm))
+    mx = float(max_norm)
     if not (mx > 0.0) or math.isinf(mx):
         return F32(1.0), True
     return F32(min(1.0, mx / (norm + 1e-6))), True

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element, on the same seeded inputs.
+
+Tolerances: FP32 states and the norm within 1e-6 relative (floor 1e-6 of
+the tensor's RMS), the BF16 copy within 1e-2 relative, the ownership table
+bit-exact.  Both sides execute the same FP32 operations in the same order,
+so the expected outcome is bit-identical states; the count of differing
+elements is printed and, for the small cases, required to be zero.
+"""
+import math
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.method as M
+from gradient_reduction_optimizer_amd import binding as B
+from gradient_reduction_optimizer_amd import synth
+from gradient_reduction_optimizer_amd.buffers import DeviceState, Plan
+from gpu_harness import (BF16_RTOL, FP32_RTOL, Case, Compare, assert_parity, bits16, host,
+                         run_parity)
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _spec(pid, shape, placement, shard_index=None, frozen=False, no_decay=False):
+    if shard_index is None:
+        shard_index = 0 if placement == "shard" else -1
+    return synth.TensorSpec(pid, f"t{pid}", tuple(shape), placement, shard_index=shard_index,
+                            frozen=frozen, no_decay=no_decay)
+
+
+def ragged_workload(R=2, seed=7, bucket_elems=25_000_000, sizes=None):
+    """Odd-sized tensors of every placement spanning several chunks, plus a
+    frozen and a no-decay tensor."""
+    rng = np.random.default_rng(seed)
+    if sizes is None:
+        sizes = [1, 7, 8, 9, 63, 65, 1000, 16383, 16384, 16385, 40000, 70001, 3 * 16384 + 5]
+    tensors = []
+    for i, n in enumerate(sizes):
+        pl = synth.PLACEMENTS[i % 4]
+        tensors.append(_spec(i, (n,), pl, shard_index=(i % R) if pl == "shard" else -1,
+                             no_decay=(i % 5 == 3)))
+    tensors.append(_spec(len(sizes), (33, 17), "replicate", frozen=True))
+    tensors.append(_spec(len(sizes) + 1, (0, 4), "partial"))
+    return synth.Workload("ragged", tensors, R=R, windows=[3], sigma=1e-2, seed=seed,
+                          bucket_elems=bucket_elems)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu):
+    torch.cuda.synchronize()
+    yield
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------- tiny sets
+@pytest.mark.parametrize("name", ["tiny", "tiny-literal"])
+def test_tiny_parity_bit_exact(name):
+    w = synth.WORKLOADS[name]()
+    log(f"case {name} windows [1, 3, 2]")
+    _, cmps, norms = run_parity(w, [1, 3, 2], log=log)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+
+
+def test_tiny_small_buckets_split_tensors():
+    w = synth.tiny(bucket_elems=4096)
+    log("case tiny bucket_elems=4096")
+    c, cmps, norms = run_parity(w, [2, 1], log=log)
+    assert c.plan.info["n_buckets"] > 8
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8])
+def test_ragged_sizes_every_R(R):
+    w = ragged_workload(R=R)
+    log(f"case ragged R={R}")
+    _, cmps, norms = run_parity(w, [3, 4, 1], log=log)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+
+
+def test_more_than_64_buckets_per_call():
+    w = ragged_workload(bucket_elems=64, sizes=[5000, 3, 64, 129, 777])
+    log("case ragged bucket_elems=64 (many launches per call)")
+    c, cmps, norms = run_parity(w, [2], log=log)
+    assert c.plan.info["n_buckets"] > 64
+    assert_parity(cmps, norms)
+
+
+def test_unfused_and_per_bucket_calls_give_identical_bits():
+    w = ragged_workload(bucket_elems=20000)
+    log("case fused vs unfused vs per-bucket calls")
+    ca, _, na = run_parity(w, [3, 2], fuse=True, log=log)
+    cb, _, nb_ = run_parity(w, [3, 2], fuse=False, log=log)
+    nbk = ca.plan.info["n_buckets"]
+    cc, _, nc = run_parity(w, [3, 2], fuse=True, bucket_order=list(range(nbk))[::-1], log=log)
+    for x in (cb, cc):
+        for arr in ("acc", "master", "m", "v"):
+            assert torch.equal(getattr(ca.st, arr).view(torch.int32), getattr(x.st, arr).view(torch.int32)), arr
+        assert torch.equal(ca.st.p_bf16.view(torch.int16), x.st.p_bf16.view(torch.int16))
+    assert [n[0] for n in na] == [n[0] for n in nb_] == [n[0] for n in nc]
+
+
+@pytest.mark.parametrize("max_norm", [0.0, float("inf"), -1.0, 1e-3, 1e9])
+def test_clip_settings(max_norm):
+    w = synth.tiny()
+    log(f"case tiny max_norm={max_norm}")
+    _, cmps, norms = run_parity(w, [2], max_norm=max_norm, log=log)
+    assert_parity(cmps, norms)
+
+
+def test_repeat_runs_are_bit_identical():
+    w = synth.tiny(literal=True)
+    a, _, na = run_parity(w, [2, 3], log=log)
+    b, _, nb_ = run_parity(w, [2, 3], log=log)
+    assert [x[0] for x in na] == [x[0] for x in nb_]
+    for arr in ("acc", "master", "m", "v"):
+        assert torch.equal(getattr(a.st, arr).view(torch.int32), getattr(b.st, arr).view(torch.int32))
+
+
+# ----------------------------------------------------------- edge cases
+def test_nonfinite_gradient_skips_the_step():
+    w = ragged_workload()
+    c = Case(w)
+    before = {k: getattr(c.st, k).clone() for k in ("master", "m", "v", "p_bf16")}
+    g = c.draw(1, 0)
+    i = next(j for j, x in enumerate(g) if x is not None and x[0].numel() > 100)
+    g[i][0][37] = float("nan")
+    c.gpu_accumulate(g, 0, 1)
+    norm, norm_sq, finite = c.gpu_finish(1, 1, 1.0)
+    log(f"nan case: norm={norm} finite={finite}")
+    assert not finite and math.isnan(norm)
+    for k, t in before.items():
+        assert torch.equal(getattr(c.st, k).view(torch.int16 if k == "p_bf16" else torch.int32),
+                           t.view(torch.int16 if k == "p_bf16" else torch.int32)), k
+    # the next window works normally
+    g = c.draw(2, 0)
+    c.gpu_accumulate(g, 0, 1)
+    norm, _, finite = c.gpu_finish(1, 1, 1.0)
+    assert finite and math.isfinite(norm)
+    # an infinity is reported the same way
+    g = c.draw(3, 0)
+    g[i][0][5] = float("inf")
+    c.gpu_accumulate(g, 0, 1)
+    norm, _, finite = c.gpu_finish(1, 2, 1.0)
+    assert not finite
+
+
+def test_empty_and_all_frozen_plans():
+    for tensors in ([], [_spec(1, (100,), "replicate", frozen=True), _spec(2, (0,), "shard")]):
+        plan = Plan(tensors, 2, 1 << 20)
+        st = DeviceState(plan)
+        s = torch.cuda.current_stream().cuda_stream
+        B.gro_accumulate(plan.handle, 0, 0, [], st.acc.data_ptr(), 0, 1, s)
+        B.gro_reduce_norm(plan.handle, st.acc.data_ptr(), 1, s)
+        norm, sq, finite = B.gro_plan_get_norm(plan.handle)
+        assert norm == 0.0 and sq == 0.0 and finite
+        B.gro_clip_adamw(plan.handle, st.acc.data_ptr(), 1, 1.0,
+                         dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), 1,
+                         st.master.data_ptr(), st.m.data_ptr(), st.v.data_ptr(), st.p_bf16.data_ptr(), s)
+        torch.cuda.synchronize()
+
+
+def test_bf16_copy_rounding_edge_classes():
+    """With lr = 0 and no decay the update leaves p unchanged, so the BF16
+    copy is RNE(p) for arbitrary FP32 bit patterns fed in as the master."""
+    hi = np.arange(0, 65536, 7, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    pats = (hi[:, None] | lows[None, :]).ravel()
+    pats = np.concatenate([pats, np.array([0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x00008000,
+                                           0x7F800000, 0xFF800000, 0x7FC00000, 0x00000001], np.uint32)])
+    x = pats.view(np.float32)
+    n = x.size
+    w = synth.Workload("bf16-edges", [_spec(0, (n,), "reduced")], R=1, windows=[1], sigma=0.0, seed=0,
+                       bucket_elems=1 << 24, lr=0.0, weight_decay=0.0)
+    plan = Plan(w.tensors, 1, w.bucket_elems)
+    st = DeviceState(plan)
+    st.flat_view(st.master, 0).copy_(torch.from_numpy(x.copy()))
+    bufs = st.grad_buffers()  # zero gradients
+    s = torch.cuda.current_stream().cuda_stream
+    B.gro_accumulate(plan.handle, 0, 1, [bufs[0].data_ptr()], st.acc.data_ptr(), 0, 1, s)
+    B.gro_reduce_norm(plan.handle, st.acc.data_ptr(), 1, s)
+    B.gro_clip_adamw(plan.handle, st.acc.data_ptr(), 1, 0.0, w.hparams, 1, st.master.data_ptr(),
+                     st.m.data_ptr(), st.v.data_ptr(), st.p_bf16.data_ptr(), s)
+    got = bits16(st.flat_view(st.p_bf16, 0))
+    want = M.f32_to_bf16(x)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.isnan(M.bf16_to_f32(got[nan])).all()
+    master = host(st.flat_view(st.master, 0))
+    fin = np.isfinite(x)
+    assert np.array_equal(master[fin].view(np.uint32), x[fin].view(np.uint32))
+
+
+def test_window_bookkeeping_errors():
+    w = synth.tiny()
+    c = Case(w)
+    s = c.stream
+    nb = c.plan.info["n_buckets"]
+    ptrs = [b.data_ptr() for b in c.bufs]
+    h = c.plan.handle
+    acc = c.st.acc.data_ptr()
+    with pytest.raises(B.GroError) as e:      # skipping microbatch 0
+        B.gro_accumulate(h, 0, nb, ptrs, acc, 1, 2, s)
+    assert e.value.kind == "state"
+    B.gro_accumulate(h, 0, nb, ptrs, acc, 0, 2, s)
+    with pytest.raises(B.GroError) as e:      # window not complete
+        B.gro_reduce_norm(h, acc, 2, s)
+    assert e.value.kind == "state"
+    with pytest.raises(B.GroError) as e:      # clip before norm
+        B.gro_clip_adamw(h, acc, 1, 1.0, w.hparams, 1, c.st.master.data_ptr(), c.st.m.data_ptr(),
+                         c.st.v.data_ptr(), 0, s)
+    assert e.value.kind == "state"
+    with pytest.raises(B.GroError) as e:      # misaligned pointer
+        B.gro_accumulate(h, 0, nb, ptrs, acc + 4, 1, 2, s)
+    assert e.value.kind == "invalid"
+    B.gro_accumulate(h, 0, nb, ptrs, acc, 1, 2, s)
+    with pytest.raises(B.GroError) as e:      # window-size mismatch
+        B.gro_reduce_norm(h, acc, 3, s)
+    assert e.value.kind == "state"
+    B.gro_reduce_norm(h, acc, 2, s)
+    with pytest.raises(B.GroError) as e:      # bad step
+        B.gro_clip_adamw(h, acc, 2, 1.0, w.hparams, 0, c.st.master.data_ptr(), c.st.m.data_ptr(),
+                         c.st.v.data_ptr(), 0, s)
+    assert e.value.kind == "invalid"
+    with pytest.raises(B.GroError) as e:      # NaN max_norm
+        B.gro_clip_adamw(h, acc, 2, float("nan"), w.hparams, 1, c.st.master.data_ptr(), c.st.m.data_ptr(),
+                         c.st.v.data_ptr(), 0, s)
+    assert e.value.kind == "invalid"
+    B.gro_clip_adamw(h, acc, 2, 1.0, w.hparams, 1, c.st.master.data_ptr(), c.st.m.data_ptr(),
+                     c.st.v.data_ptr(), 0, s)
+    with pytest.raises(B.GroError) as e:      # the window was consumed
+        B.gro_reduce_norm(h, acc, 2, s)
+    assert e.value.kind == "state"
+    torch.cuda.synchronize()

@@ -1,0 +1,227 @@
+"""Host-side tests of the C-ABI library (no GPU needed): symbol exports,
+the ownership table against the oracle (bit-exact), layout invariants and
+fail-before-fit validation.  Only host-only entry points are called."""
+import os
+import re
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+
+import oracle.method as M
+from gradient_reduction_optimizer_amd import binding as B
+from gradient_reduction_optimizer_amd import synth
+from gradient_reduction_optimizer_amd.buffers import Plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CHUNK = 16384
+ALIGN = 64
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gro.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gro_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = B.load()
+    declared = header_functions()
+    assert declared, "no functions found in include/gro.h"
+    assert set(declared) == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def _oracle_rows(tensors, R):
+    return M.assign_owners(tensors, R)
+
+
+def _check_table(tensors, R, bucket_elems):
+    plan = Plan(tensors, R, bucket_elems)
+    rows = _oracle_rows(tensors, R)
+    assert len(plan.tensors) == len(rows)
+    for t, o in zip(plan.tensors, rows):
+        got = (t["param_id"], B.OWNER_NAMES[t["owner"]], t["slots"], t["divisor"],
+               bool(t["in_norm"]), bool(t["updated"]), bool(t["decayed"]))
+        want = (o.param_id, o.owner, o.slots, o.divisor, o.in_norm, o.updated, o.decayed)
+        assert got == want
+    _check_layout(plan, tensors, bucket_elems)
+    return plan
+
+
+def _check_layout(plan, tensors, cap):
+    info, buckets = plan.info, plan.buckets
+    # chunks partition each bucket; buckets are disjoint, aligned, ordered
+    q = 0
+    end = 0
+    covered = 0
+    for bk in buckets:
+        assert bk["flat_base"] % ALIGN == 0 and bk["flat_base"] >= end
+        assert 0 < bk["len"] <= cap
+        assert bk["slot_stride"] % ALIGN == 0 and bk["slot_stride"] >= bk["len"]
+        assert bk["first_chunk"] == q and bk["n_chunks"] == -(-bk["len"] // CHUNK)
+        q += bk["n_chunks"]
+        end = bk["flat_base"] + bk["len"]
+        covered += bk["len"]
+    assert info["n_chunks"] == q
+    assert info["n_owned"] == covered
+    assert info["n_flat"] % ALIGN == 0 and info["n_flat"] >= end
+    # every owned element belongs to exactly one tensor: no parameter is
+    # reduced twice and nothing is missed (interval bookkeeping)
+    spans = []
+    for i, t in enumerate(plan.tensors):
+        if not t["updated"] or t["numel"] == 0:
+            assert t["flat_offset"] == -1 and t["n_buckets"] == 0
+            continue
+        spans.append((t["flat_offset"], t["flat_offset"] + t["numel"]))
+        segs = plan.segments(i)
+        assert sum(s[3] for s in segs) == t["numel"]
+        for b, _, _, _ in segs:
+            bk = buckets[b]
+            assert bk["owner"] == t["owner"] and bk["decayed"] == t["decayed"] and bk["slots"] == t["slots"]
+        # only tensors larger than the capacity are split
+        assert (t["n_buckets"] > 1) == (t["numel"] > cap)
+    spans.sort()
+    for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+        assert a1 <= b0, "two tensors overlap"
+    merged = []
+    for a, b in spans:
+        if merged and merged[-1][1] == a:
+            merged[-1][1] = b
+        else:
+            merged.append([a, b])
+    bmerged = []
+    for bk in buckets:
+        a, b = bk["flat_base"], bk["flat_base"] + bk["len"]
+        if bmerged and bmerged[-1][1] == a:
+            bmerged[-1][1] = b
+        else:
+            bmerged.append([a, b])
+    assert merged == bmerged, "tensors do not exactly cover the buckets"
+    # owner classes appear in the fixed order MEAN, SUM, LOCAL_SHARD, LOCAL_REDUCED
+    keys = [(bk["owner"], -bk["decayed"]) for bk in buckets]
+    assert keys == sorted(keys)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny-literal", "draft-67m", "draft-67m-tp2-half",
+                                  "dense-1b-fsdp8-shard", "dense-8b-share"])
+def test_ownership_matches_oracle(name):
+    w = synth.WORKLOADS[name]()
+    _check_table(w.tensors, w.R, w.bucket_elems)
+
+
+def test_hybrid_ownership_matches_oracle():
+    w = synth.hybrid_moe()
+    plan = _check_table(w.tensors, w.R, w.bucket_elems)
+    assert plan.info["n_owned"] == w.numel
+
+
+def test_golden_tiny_table_through_the_library():
+    from oracle_pins import read_golden_ownership
+    gold = read_golden_ownership()
+    w = synth.tiny()
+    plan = Plan(w.tensors, w.R, w.bucket_elems)
+    for g, t in zip(gold, plan.tensors):
+        assert (B.OWNER_NAMES[t["owner"]], t["slots"], t["divisor"]) == (g["owner"], g["slots"], g["divisor"])
+
+
+@pytest.mark.parametrize("cap", [64, 100, 4096, 5000, 65536])
+def test_small_bucket_caps_split_large_tensors(cap):
+    w = synth.tiny(bucket_elems=cap)
+    plan = _check_table(w.tensors, w.R, cap)
+    assert plan.info["n_buckets"] > 4
+
+
+def _spec(pid, shape, placement, shard_index=None, frozen=False, no_decay=False):
+    if shard_index is None:
+        shard_index = 0 if placement == "shard" else -1
+    return SimpleNamespace(param_id=pid, shape=tuple(shape), placement=placement,
+                           shard_index=shard_index, frozen=frozen, no_decay=no_decay)
+
+
+def test_random_descriptor_sets_match_oracle():
+    rng = np.random.default_rng(123)
+    for trial in range(60):
+        R = int(rng.integers(1, 9))
+        n = int(rng.integers(0, 40))
+        tensors = []
+        for i in range(n):
+            nd = int(rng.integers(0, 4))
+            shape = tuple(int(x) for x in rng.integers(0, 70, size=nd))
+            pl = synth.PLACEMENTS[int(rng.integers(0, 4))]
+            tensors.append(_spec(int(rng.integers(0, 1 << 40)) * 64 + i, shape, pl,
+                                 shard_index=int(rng.integers(0, R)) if pl == "shard" else -1,
+                                 frozen=bool(rng.random() < 0.1), no_decay=bool(rng.random() < 0.3)))
+        cap = int(rng.choice([64, 128, 200, 1000, 1 << 20]))
+        _check_table(tensors, R, cap)
+
+
+def test_layout_is_deterministic():
+    w = synth.hybrid_moe()
+    a = Plan(w.tensors, w.R, w.bucket_elems)
+    b = Plan(w.tensors, w.R, w.bucket_elems)
+    assert a.tensors == b.tensors and a.buckets == b.buckets and a.info == b.info
+
+
+REJECTIONS = [
+    ([_spec(1, (3,), "shard"), _spec(1, (3,), "replicate")], 2, "duplicate"),
+    ([_spec(1, (3,), "replicate")], 0, "invalid"),
+    ([_spec(1, (3,), "shard", shard_index=2)], 2, "placement"),
+    ([_spec(1, (3,), "shard", shard_index=-1)], 2, "placement"),
+    ([_spec(1, (3,), "partial", shard_index=0)], 2, "placement"),
+    ([_spec(1, (3,), "sharded")], 2, "placement"),
+    ([_spec(1, (3, -1), "replicate")], 2, "invalid"),
+]
+
+
+@pytest.mark.parametrize("tensors,R,kind", REJECTIONS)
+def test_rejections_match_oracle(tensors, R, kind):
+    with pytest.raises(M.Rejected) as eo:
+        M.assign_owners(tensors, R)
+    assert eo.value.kind == kind
+    with pytest.raises(B.GroError) as eg:
+        B.gro_plan_create(tensors, R, 1 << 20)
+    assert eg.value.kind == kind
+
+
+def test_invalid_plan_arguments():
+    with pytest.raises(B.GroError) as e:
+        B.gro_plan_create([_spec(1, (3,), "replicate")], 2, 63)
+    assert e.value.kind == "invalid"
+    with pytest.raises(B.GroError) as e:
+        B.gro_plan_create([dict(param_id=1, shape=(2,) * 9, placement="replicate", shard_index=-1)], 2, 1 << 20)
+    assert e.value.kind == "invalid"
+    with pytest.raises(B.GroError) as e:
+        B.gro_plan_create([dict(param_id=1, shape=(4,), placement="replicate", shard_index=-1, flags=8)], 2, 1 << 20)
+    assert e.value.kind == "placement"
+    with pytest.raises(B.GroError) as e:
+        B.gro_plan_create([dict(param_id=1, shape=(1 << 30, 1 << 30), placement="replicate", shard_index=-1)],
+                          2, 1 << 20)
+    assert e.value.kind == "invalid"
+
+
+def test_empty_and_excluded_plans():
+    p = Plan([], 2, 1 << 20)
+    assert p.info["n_buckets"] == 0 and p.info["n_flat"] == 0 and p.info["workspace_bytes"] > 0
+    p = Plan([_spec(1, (5,), "replicate", frozen=True), _spec(2, (0, 3), "shard")], 2, 1 << 20)
+    assert p.info["n_buckets"] == 0 and p.info["n_owned"] == 0
+    assert p.tensors[0]["owner"] == B.GRO_OWNER_EXCLUDED
+
+
+def test_unbound_plan_calls_fail_before_device_work():
+    w = synth.tiny()
+    plan = Plan(w.tensors, w.R, w.bucket_elems)
+    with pytest.raises(B.GroError) as e:
+        B.gro_accumulate(plan.handle, 0, 1, [1 << 20], 1 << 20, 0)
+    assert e.value.kind == "state"
+    with pytest.raises(B.GroError) as e:
+        B.gro_reduce_norm(plan.handle, 1 << 20, 1)
+    assert e.value.kind == "state"
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    with pytest.raises(B.GroError) as e:
+        B.gro_clip_adamw(plan.handle, 1 << 20, 1, 1.0, hp, 1, 1 << 20, 1 << 20, 1 << 20)
+    assert e.value.kind == "state"
+    with pytest.raises(B.GroError) as e:
+        B.gro_plan_get_norm(plan.handle)
+    assert e.value.kind == "state"
