@@ -36,6 +36,9 @@ def parse():
                     help="fraction of the workload's elements the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the benchmark, run a plain device copy of this many MiB three times "
+                         "(the calibration kernel for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -119,11 +122,12 @@ def main():
     # Inputs resident in HBM: one set of BF16 bucket buffers per microbatch.
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(synth.stream_seed(w.seed, 99))
-    grads = []
+    grad_tensors, grads = [], []  # keep the tensors alive: the library only gets pointers
     for k in range(n):
         bufs = st.grad_buffers()
         for b in bufs:
             b.copy_((torch.randn(b.shape, generator=gen, device="cuda:0") * w.sigma).to(torch.bfloat16))
+        grad_tensors.append(bufs)
         grads.append([b.data_ptr() for b in bufs])
     st.master.copy_(torch.randn(st.master.shape, generator=gen, device="cuda:0") * w.master_sigma)
     nb = info["n_buckets"]
@@ -164,19 +168,18 @@ def main():
     for _ in range(args.warmup):
         one_step(False)
     torch.cuda.synchronize()
-    # Wall-clock timed region: exactly `steps` steps, no events inside.
+    # Timed region: exactly `steps` steps.  HIP events recorded on the launch
+    # stream around each call give the per-kernel durations (a stream marker
+    # costs a few microseconds at most).
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step(False)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    # Per-kernel durations with HIP events on the launch stream (a separate
-    # pass of the same steps so the wall-clock figure carries no events).
     for _ in range(args.steps):
         one_step(True)
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
     norm, _, finite = B.gro_plan_get_norm(plan.handle)
+    if not finite:
+        raise RuntimeError("the benchmark's norm is not finite: the timed steps skipped the update")
 
     def avg_ms(pairs):
         return sum(a.elapsed_time(b) for a, b in pairs) / max(len(pairs), 1)
@@ -229,6 +232,15 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_frac, log)
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe"] = {"bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}
     print(json.dumps(out), flush=True)
 
 

@@ -1,11 +1,14 @@
 // gfx950 (MI355X, CDNA4) kernels for the gradient-ownership hot path.
 //
 // Every pass is a multi-tensor walk over the plan's chunk table: one
-// 256-lane workgroup per chunk of up to kChunkElems elements, where a chunk
-// lies inside one bucket and so has one owner class.  Lanes move 8 elements
-// at a time with 128-bit loads and stores (8 BF16 or 4+4 FP32), two such
-// vectors in flight per lane.  The path is bound by HBM bandwidth, not by a
-// contraction, so there is no MFMA here.
+// workgroup per chunk of up to kChunkElems elements, where a chunk lies
+// inside one bucket and so has one owner class.  A lane owns 4-element
+// vectors v = lane, lane + kBlock, lane + 2*kBlock, ... of its chunk, so
+// every memory instruction of a wave covers one contiguous range: 1 KB of
+// FP32 (a 128-bit access per lane) or 512 B of BF16 (64-bit per lane).
+// kUnroll vectors per lane are loaded before any is consumed, to keep enough
+// bytes in flight to cover HBM latency.  The path is bound by HBM bandwidth,
+// not by a contraction, so there is no MFMA here.
 //
 // Arithmetic follows NeMo Automodel issue #3857, "refactor(distributed):
 // establish shared native TP replica ownership" ("Why this needs separate
@@ -27,11 +30,27 @@
 namespace gro {
 namespace {
 
-constexpr int kBlock = 256;            // lanes per workgroup (4 waves of 64)
+// Launch-shape knobs (compile-time; the chunking itself is fixed by the
+// plan).  The norm's per-chunk summation order depends on kBlock, so a
+// build has one fixed value.
+#ifndef GRO_BLOCK
+#define GRO_BLOCK 256
+#endif
+#ifndef GRO_UNROLL
+#define GRO_UNROLL 2
+#endif
+
+constexpr int kBlock = GRO_BLOCK;      // lanes per workgroup (waves of 64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kUnroll = 2;             // 8-element vectors in flight per lane
+constexpr int kUnroll = GRO_UNROLL;    // 4-element vectors in flight per lane
 constexpr int kFinalBlock = 1024;      // the norm's second stage
-static_assert(kChunkElems % (8 * kBlock) == 0, "chunks are whole workgroup tiles");
+static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
+static_assert(kChunkElems % (4 * kBlock) == 0, "chunks are whole workgroup tiles");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // x / d for a positive integer d.  When d is a power of two its reciprocal
 // is exact and x * (1/d) is the same correctly rounded value as x / d, so
@@ -54,34 +73,47 @@ __device__ __forceinline__ float divide(float x, const Divisor& q) {
   return q.pow2 ? x * q.inv : x / q.d;
 }
 
-__device__ __forceinline__ void widen8(const uint4 r, float (&x)[8]) {
-  x[0] = __uint_as_float(r.x << 16);
-  x[1] = __uint_as_float(r.x & 0xffff0000u);
-  x[2] = __uint_as_float(r.y << 16);
-  x[3] = __uint_as_float(r.y & 0xffff0000u);
-  x[4] = __uint_as_float(r.z << 16);
-  x[5] = __uint_as_float(r.z & 0xffff0000u);
-  x[6] = __uint_as_float(r.w << 16);
-  x[7] = __uint_as_float(r.w & 0xffff0000u);
+// The same choice made at compile time, for the branch-free full-chunk paths:
+// kNoDiv (nothing to divide), kMulInv (power-of-two divisor), kIeeeDiv.
+enum DivMode { kNoDiv = 0, kMulInv = 1, kIeeeDiv = 2 };
+__host__ __device__ inline int div_mode(const Divisor& q) { return q.pow2 ? kMulInv : kIeeeDiv; }
+template <int M>
+__device__ __forceinline__ float divide_m(float x, const Divisor& q) {
+  if constexpr (M == kMulInv) return x * q.inv;
+  else if constexpr (M == kIeeeDiv) return x / q.d;
+  else return x;
+}
+
+// Four BF16 (two 32-bit words, element 0 in the low half) widened exactly.
+__device__ __forceinline__ f32x4 widen4(const u32x2 r) {
+  f32x4 x;
+  x.x = __uint_as_float(r.x << 16);
+  x.y = __uint_as_float(r.x & 0xffff0000u);
+  x.z = __uint_as_float(r.y << 16);
+  x.w = __uint_as_float(r.y & 0xffff0000u);
+  return x;
 }
 
 __device__ __forceinline__ float widen1(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// FP32 -> BF16, round to nearest even (gfx950 converts in hardware).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const __bf16 h = static_cast<__bf16>(x);
-  return uint32_t(__builtin_bit_cast(uint16_t, h));
+// FP32 -> BF16, round to nearest even, two per v_cvt_pk_bf16_f32:
+// lo in bits 0..15, hi in 16..31.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-__device__ __forceinline__ uint4 ld4u(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ float4 ld4f(const float* p) { return *reinterpret_cast<const float4*>(p); }
-__device__ __forceinline__ void st4f(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
+__device__ __forceinline__ u32x2 ld2u(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4f(float* p, const f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st2u(uint16_t* p, const u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
 // Sum over the workgroup in a fixed order: a wave64 butterfly (every lane
-// ends with the same bits because IEEE addition commutes), then the four
-// wave totals in wave order.  Returned in every lane.
+// ends with the same bits because IEEE addition commutes), then the wave
+// totals in wave order.  Returned in every lane.
 __device__ double block_sum(double x) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
@@ -99,6 +131,11 @@ __device__ __forceinline__ int64_t chunk_of_block(int64_t q_begin) {
   return q_begin - (q_begin & 7) + int64_t(blockIdx.x);
 }
 
+__device__ __forceinline__ double sq(float x) {
+  const double d = double(x);
+  return d * d;
+}
+
 // ------------------------------------------------------------ accumulate
 struct AccChunk {
   const uint16_t* g;   // slot 0 of this chunk in the bucket's gradient buffer
@@ -113,132 +150,143 @@ struct AccChunk {
   Divisor wdiv;        // window length, for the norm
 };
 
+// One element's reduction: slots summed in slot order, then /R for MEAN.
+// (The vector path below performs exactly these operations lane-wise.)
+__device__ __forceinline__ float reduce1(const AccChunk& c, int i) {
+  float s = widen1(c.g[i]);
+  for (int r = 1; r < c.slots; ++r) s = s + widen1(c.g[int64_t(r) * c.stride + i]);
+  return c.mean ? divide(s, c.rdiv) : s;
+}
+
+// Ragged tail [4*nvec, len): handled by the lane that owns vector nvec, after
+// its full vectors, so the lane's element order stays ascending.
+__device__ __forceinline__ double accumulate_tail(const AccChunk& c, int nvec) {
+  double ss = 0.0;
+  if ((c.len & 3) && int(threadIdx.x) == nvec % kBlock) {
+    for (int i = nvec * 4; i < c.len; ++i) {
+      float s = reduce1(c, i);
+      if (!c.first) s = c.acc[i] + s;
+      c.acc[i] = s;
+      if (c.fuse) ss += sq(divide(s, c.wdiv));
+    }
+  }
+  return ss;
+}
+
 // Per element: widen the slots, sum them in slot order, divide by R for
 // MEAN, then start or extend the accumulator.  Returns this lane's FP64 sum
-// of (acc/window)^2 over its elements (0 unless fuse), taken in the lane's
-// element order: vectors t, t+256, ... then, for the lane that owns vector
-// len/8, the ragged tail.
+// of (acc/window)^2 over its elements (0 unless fuse), in the lane's element
+// order: its vectors in ascending order, each vector's elements in order,
+// then the tail.  C = slot count known at compile time (0 = runtime).
 template <int C>
-__device__ double accumulate_chunk(const AccChunk& c) {
-  const int nvec = c.len >> 3;
+__device__ double accumulate_generic(const AccChunk& c) {
+  constexpr int kC = C > 0 ? C : 1;
+  const int nvec = c.len >> 2;
   double ss = 0.0;
   for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    uint4 raw[kUnroll][C];
-    float4 old[kUnroll][2];
+    f32x4 red[kUnroll];
+    f32x4 old[kUnroll];
+    // Issue every load of this round before using any.
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int v = v0 + u * kBlock;
       if (v < nvec) {
+        if (C > 0) {
+          u32x2 raw[kC];
 #pragma unroll
-        for (int r = 0; r < C; ++r) raw[u][r] = ld4u(c.g + r * c.stride + 8 * v);
-        if (!c.first) {
-          old[u][0] = ld4f(c.acc + 8 * v);
-          old[u][1] = ld4f(c.acc + 8 * v + 4);
+          for (int r = 0; r < kC; ++r) raw[r] = ld2u(c.g + int64_t(r) * c.stride + 4 * v);
+          red[u] = widen4(raw[0]);
+#pragma unroll
+          for (int r = 1; r < kC; ++r) red[u] = red[u] + widen4(raw[r]);
+        } else {
+          red[u] = widen4(ld2u(c.g + 4 * v));
+          for (int r = 1; r < c.slots; ++r) red[u] = red[u] + widen4(ld2u(c.g + int64_t(r) * c.stride + 4 * v));
         }
+        if (!c.first) old[u] = ld4f(c.acc + 4 * v);
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int v = v0 + u * kBlock;
       if (v < nvec) {
-        float s[8];
-        widen8(raw[u][0], s);
-#pragma unroll
-        for (int r = 1; r < C; ++r) {
-          float x[8];
-          widen8(raw[u][r], x);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
-        }
+        f32x4 s = red[u];
         if (c.mean) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[e] = divide(s[e], c.rdiv);
+          s.x = divide(s.x, c.rdiv);
+          s.y = divide(s.y, c.rdiv);
+          s.z = divide(s.z, c.rdiv);
+          s.w = divide(s.w, c.rdiv);
         }
-        if (!c.first) {
-          s[0] = old[u][0].x + s[0];
-          s[1] = old[u][0].y + s[1];
-          s[2] = old[u][0].z + s[2];
-          s[3] = old[u][0].w + s[3];
-          s[4] = old[u][1].x + s[4];
-          s[5] = old[u][1].y + s[5];
-          s[6] = old[u][1].z + s[6];
-          s[7] = old[u][1].w + s[7];
-        }
-        st4f(c.acc + 8 * v, s[0], s[1], s[2], s[3]);
-        st4f(c.acc + 8 * v + 4, s[4], s[5], s[6], s[7]);
+        if (!c.first) s = old[u] + s;
+        st4f(c.acc + 4 * v, s);
         if (c.fuse) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double gq = double(divide(s[e], c.wdiv));
-            ss += gq * gq;
-          }
+          ss += sq(divide(s.x, c.wdiv));
+          ss += sq(divide(s.y, c.wdiv));
+          ss += sq(divide(s.z, c.wdiv));
+          ss += sq(divide(s.w, c.wdiv));
         }
       }
     }
   }
-  if ((c.len & 7) && int(threadIdx.x) == nvec % kBlock) {
-    for (int i = nvec * 8; i < c.len; ++i) {
-      float s = widen1(c.g[i]);
-      for (int r = 1; r < c.slots; ++r) s = s + widen1(c.g[r * c.stride + i]);
-      if (c.mean) s = divide(s, c.rdiv);
-      if (!c.first) s = c.acc[i] + s;
-      c.acc[i] = s;
-      if (c.fuse) {
-        const double gq = double(divide(s, c.wdiv));
-        ss += gq * gq;
+  return ss + accumulate_tail(c, nvec);
+}
+
+// A full chunk (len == kChunkElems) with every choice fixed at compile time:
+// C slots, RM how the slot sum is divided (kNoDiv, or kMulInv for MEAN at
+// R = 2), FIRST whether the window starts here, WM the window division for
+// the fused norm (kNoDiv = no norm).  Same operations, same order as
+// accumulate_generic, without bounds checks or per-element branches.
+template <int C, int RM, bool FIRST, int WM>
+__device__ double accumulate_full(const AccChunk& c) {
+  constexpr int nvec = kChunkElems / 4;
+  static_assert(nvec % (kUnroll * kBlock) == 0, "full chunks are whole rounds");
+  double ss = 0.0;
+#pragma unroll 1
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    f32x4 red[kUnroll];
+    f32x4 old[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      u32x2 raw[C];
+#pragma unroll
+      for (int r = 0; r < C; ++r) raw[r] = ld2u(c.g + int64_t(r) * c.stride + 4 * v);
+      if (!FIRST) old[u] = ld4f(c.acc + 4 * v);
+      red[u] = widen4(raw[0]);
+#pragma unroll
+      for (int r = 1; r < C; ++r) red[u] = red[u] + widen4(raw[r]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      f32x4 s = red[u];
+      s.x = divide_m<RM>(s.x, c.rdiv);
+      s.y = divide_m<RM>(s.y, c.rdiv);
+      s.z = divide_m<RM>(s.z, c.rdiv);
+      s.w = divide_m<RM>(s.w, c.rdiv);
+      if (!FIRST) s = old[u] + s;
+      st4f(c.acc + 4 * v, s);
+      if (WM != kNoDiv) {
+        ss += sq(divide_m<WM>(s.x, c.wdiv));
+        ss += sq(divide_m<WM>(s.y, c.wdiv));
+        ss += sq(divide_m<WM>(s.z, c.wdiv));
+        ss += sq(divide_m<WM>(s.w, c.wdiv));
       }
     }
   }
   return ss;
 }
 
-// Any slot count (R other than 1 or 2): same arithmetic and element order,
-// one vector at a time.
-__device__ double accumulate_chunk_any(const AccChunk& c) {
-  const int nvec = c.len >> 3;
-  double ss = 0.0;
-  for (int v = threadIdx.x; v < nvec; v += kBlock) {
-    float s[8];
-    widen8(ld4u(c.g + 8 * v), s);
-    for (int r = 1; r < c.slots; ++r) {
-      float x[8];
-      widen8(ld4u(c.g + r * c.stride + 8 * v), x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = s[e] + x[e];
-    }
-    if (c.mean) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = divide(s[e], c.rdiv);
-    }
-    if (!c.first) {
-      const float4 a0 = ld4f(c.acc + 8 * v), a1 = ld4f(c.acc + 8 * v + 4);
-      s[0] = a0.x + s[0]; s[1] = a0.y + s[1]; s[2] = a0.z + s[2]; s[3] = a0.w + s[3];
-      s[4] = a1.x + s[4]; s[5] = a1.y + s[5]; s[6] = a1.z + s[6]; s[7] = a1.w + s[7];
-    }
-    st4f(c.acc + 8 * v, s[0], s[1], s[2], s[3]);
-    st4f(c.acc + 8 * v + 4, s[4], s[5], s[6], s[7]);
-    if (c.fuse) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double gq = double(divide(s[e], c.wdiv));
-        ss += gq * gq;
-      }
-    }
+template <int C, int RM>
+__device__ double accumulate_full_dispatch(const AccChunk& c) {
+  const int wm = c.fuse ? div_mode(c.wdiv) : kNoDiv;
+  if (c.first) {
+    if (wm == kNoDiv) return accumulate_full<C, RM, true, kNoDiv>(c);
+    if (wm == kMulInv) return accumulate_full<C, RM, true, kMulInv>(c);
+    return accumulate_full<C, RM, true, kIeeeDiv>(c);
   }
-  if ((c.len & 7) && int(threadIdx.x) == nvec % kBlock) {
-    for (int i = nvec * 8; i < c.len; ++i) {
-      float s = widen1(c.g[i]);
-      for (int r = 1; r < c.slots; ++r) s = s + widen1(c.g[r * c.stride + i]);
-      if (c.mean) s = divide(s, c.rdiv);
-      if (!c.first) s = c.acc[i] + s;
-      c.acc[i] = s;
-      if (c.fuse) {
-        const double gq = double(divide(s, c.wdiv));
-        ss += gq * gq;
-      }
-    }
-  }
-  return ss;
+  if (wm == kNoDiv) return accumulate_full<C, RM, false, kNoDiv>(c);
+  if (wm == kMulInv) return accumulate_full<C, RM, false, kMulInv>(c);
+  return accumulate_full<C, RM, false, kIeeeDiv>(c);
 }
 
 __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P) {
@@ -258,12 +306,18 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
   c.rdiv = make_divisor(P.R);
   c.wdiv = make_divisor(P.window > 0 ? P.window : 1);
   double ss;
-  if (c.slots == 1)
-    ss = accumulate_chunk<1>(c);
+  if (c.len == kChunkElems && c.slots == 1 && !c.mean)
+    ss = accumulate_full_dispatch<1, kNoDiv>(c);
+  else if (c.len == kChunkElems && c.slots == 2 && !c.mean)
+    ss = accumulate_full_dispatch<2, kNoDiv>(c);
+  else if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2)
+    ss = accumulate_full_dispatch<2, kMulInv>(c);
+  else if (c.slots == 1)
+    ss = accumulate_generic<1>(c);
   else if (c.slots == 2)
-    ss = accumulate_chunk<2>(c);
+    ss = accumulate_generic<2>(c);
   else
-    ss = accumulate_chunk_any(c);
+    ss = accumulate_generic<0>(c);
   if (c.fuse) {
     const double t = block_sum(ss);
     if (threadIdx.x == 0) P.partials[q] = t;
@@ -271,6 +325,55 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
 }
 
 // ------------------------------------------------------- norm, stage 1
+// Lane's sum of (acc/window)^2 over its vectors of a full chunk.
+template <int WM>
+__device__ double sumsq_full(const float* acc, const Divisor& wdiv) {
+  constexpr int nvec = kChunkElems / 4;
+  double ss = 0.0;
+#pragma unroll 1
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    f32x4 a[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) a[u] = ld4f(acc + 4 * (v0 + u * kBlock));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      ss += sq(divide_m<WM>(a[u].x, wdiv));
+      ss += sq(divide_m<WM>(a[u].y, wdiv));
+      ss += sq(divide_m<WM>(a[u].z, wdiv));
+      ss += sq(divide_m<WM>(a[u].w, wdiv));
+    }
+  }
+  return ss;
+}
+
+// Same, any length, with the ragged tail.
+__device__ double sumsq_generic(const float* acc, int len, const Divisor& wdiv) {
+  const int nvec = len >> 2;
+  double ss = 0.0;
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    f32x4 a[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      if (v < nvec) a[u] = ld4f(acc + 4 * v);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      if (v < nvec) {
+        ss += sq(divide(a[u].x, wdiv));
+        ss += sq(divide(a[u].y, wdiv));
+        ss += sq(divide(a[u].z, wdiv));
+        ss += sq(divide(a[u].w, wdiv));
+      }
+    }
+  }
+  if ((len & 3) && int(threadIdx.x) == nvec % kBlock) {
+    for (int i = nvec * 4; i < len; ++i) ss += sq(divide(acc[i], wdiv));
+  }
+  return ss;
+}
+
 // Same lane/element order as the fused accumulate, so a chunk's partial is
 // the same bits whichever kernel wrote it.
 __global__ __launch_bounds__(kBlock) void k_norm_partials(const NormLaunch P) {
@@ -279,38 +382,11 @@ __global__ __launch_bounds__(kBlock) void k_norm_partials(const NormLaunch P) {
   const ChunkDev ch = P.chunks[q];
   const float* acc = P.acc + ch.begin;
   const Divisor wdiv = make_divisor(P.window);
-  const int nvec = ch.len >> 3;
-  double ss = 0.0;
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    float4 a[kUnroll][2];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int v = v0 + u * kBlock;
-      if (v < nvec) {
-        a[u][0] = ld4f(acc + 8 * v);
-        a[u][1] = ld4f(acc + 8 * v + 4);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int v = v0 + u * kBlock;
-      if (v < nvec) {
-        const float s[8] = {a[u][0].x, a[u][0].y, a[u][0].z, a[u][0].w,
-                            a[u][1].x, a[u][1].y, a[u][1].z, a[u][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double gq = double(divide(s[e], wdiv));
-          ss += gq * gq;
-        }
-      }
-    }
-  }
-  if ((ch.len & 7) && int(threadIdx.x) == nvec % kBlock) {
-    for (int i = nvec * 8; i < ch.len; ++i) {
-      const double gq = double(divide(acc[i], wdiv));
-      ss += gq * gq;
-    }
-  }
+  double ss;
+  if (ch.len == kChunkElems)
+    ss = wdiv.pow2 ? sumsq_full<kMulInv>(acc, wdiv) : sumsq_full<kIeeeDiv>(acc, wdiv);
+  else
+    ss = sumsq_generic(acc, ch.len, wdiv);
   const double t = block_sum(ss);
   if (threadIdx.x == 0) P.partials[q] = t;
 }
@@ -342,14 +418,111 @@ struct AdamScalars {
   float coef, decay, b1, b2, omb1, omb2, step_size, sbc2, eps;
 };
 
+// g = acc/n; g^ = g*coef; p = p*decay; m = b1*m + (1-b1)*g^;
+// v = b2*v + (1-b2)*(g^*g^); p = p - step_size*(m/(sqrt(v)/sqrt_bc2 + eps)).
+template <int WM>
 __device__ __forceinline__ void adamw_elem(float a, float& p, float& m, float& v, const AdamScalars& k) {
-  const float g = divide(a, k.wdiv);
+  const float g = WM == kNoDiv ? divide(a, k.wdiv) : divide_m<WM>(a, k.wdiv);
   const float gh = g * k.coef;
   p = p * k.decay;
   m = k.b1 * m + k.omb1 * gh;
   v = k.b2 * v + k.omb2 * (gh * gh);
   const float d = sqrtf(v) / k.sbc2 + k.eps;
   p = p - k.step_size * (m / d);
+}
+
+template <int WM>
+__device__ __forceinline__ void adamw4(const f32x4 a, f32x4& p, f32x4& m, f32x4& v, const AdamScalars& k) {
+  float pp[4] = {p.x, p.y, p.z, p.w}, mm[4] = {m.x, m.y, m.z, m.w}, vv[4] = {v.x, v.y, v.z, v.w};
+  const float aa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) adamw_elem<WM>(aa[e], pp[e], mm[e], vv[e], k);
+  p = f32x4{pp[0], pp[1], pp[2], pp[3]};
+  m = f32x4{mm[0], mm[1], mm[2], mm[3]};
+  v = f32x4{vv[0], vv[1], vv[2], vv[3]};
+}
+
+struct AdamChunk {
+  const float* acc;
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* pb;   // BF16 copy, may be null
+  int len;
+};
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* pb, const f32x4 p) {
+  u32x2 o;
+  o.x = bf16x2_bits(p.x, p.y);
+  o.y = bf16x2_bits(p.z, p.w);
+  st2u(pb, o);
+}
+
+// Any chunk: runtime window division, bounds checks, ragged tail.
+__device__ void adamw_generic(const AdamChunk& c, const AdamScalars& k) {
+  const int nvec = c.len >> 2;
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    f32x4 a[kUnroll], p[kUnroll], m[kUnroll], w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      if (v < nvec) {
+        a[u] = ld4f(c.acc + 4 * v);
+        p[u] = ld4f(c.p + 4 * v);
+        m[u] = ld4f(c.m + 4 * v);
+        w[u] = ld4f(c.v + 4 * v);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      if (v < nvec) {
+        adamw4<kNoDiv>(a[u], p[u], m[u], w[u], k);
+        st4f(c.p + 4 * v, p[u]);
+        st4f(c.m + 4 * v, m[u]);
+        st4f(c.v + 4 * v, w[u]);
+        if (c.pb) store_bf16x4(c.pb + 4 * v, p[u]);
+      }
+    }
+  }
+  if ((c.len & 3) && int(threadIdx.x) == nvec % kBlock) {
+    for (int i = nvec * 4; i < c.len; ++i) {
+      float p1 = c.p[i], m1 = c.m[i], v1 = c.v[i];
+      adamw_elem<kNoDiv>(c.acc[i], p1, m1, v1, k);
+      c.p[i] = p1;
+      c.m[i] = m1;
+      c.v[i] = v1;
+      if (c.pb) c.pb[i] = bf16_bits(p1);
+    }
+  }
+}
+
+// A full chunk with the window division (WM) and the BF16 copy fixed at
+// compile time: no bounds checks, no per-element branches.
+template <int WM, bool BF16>
+__device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
+  constexpr int nvec = kChunkElems / 4;
+#pragma unroll 1
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    f32x4 a[kUnroll], p[kUnroll], m[kUnroll], w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      a[u] = ld4f(c.acc + 4 * v);
+      p[u] = ld4f(c.p + 4 * v);
+      m[u] = ld4f(c.m + 4 * v);
+      w[u] = ld4f(c.v + 4 * v);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kBlock;
+      adamw4<WM>(a[u], p[u], m[u], w[u], k);
+      st4f(c.p + 4 * v, p[u]);
+      st4f(c.m + 4 * v, m[u]);
+      st4f(c.v + 4 * v, w[u]);
+      if (BF16) store_bf16x4(c.pb + 4 * v, p[u]);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void k_adamw(const AdamWLaunch P) {
@@ -374,61 +547,24 @@ __global__ __launch_bounds__(kBlock) void k_adamw(const AdamWLaunch P) {
   k.sbc2 = P.sqrt_bc2;
   k.eps = P.eps;
 
-  const float* acc = P.acc + ch.begin;
-  float* pm = P.master + ch.begin;
-  float* mm = P.m + ch.begin;
-  float* vm = P.v + ch.begin;
-  uint16_t* pb = P.p_bf16 ? P.p_bf16 + ch.begin : nullptr;
-  const int nvec = ch.len >> 3;
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    float4 a[kUnroll][2], p[kUnroll][2], m[kUnroll][2], w[kUnroll][2];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int v = v0 + u * kBlock;
-      if (v < nvec) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          a[u][h] = ld4f(acc + 8 * v + 4 * h);
-          p[u][h] = ld4f(pm + 8 * v + 4 * h);
-          m[u][h] = ld4f(mm + 8 * v + 4 * h);
-          w[u][h] = ld4f(vm + 8 * v + 4 * h);
-        }
-      }
+  AdamChunk c;
+  c.acc = P.acc + ch.begin;
+  c.p = P.master + ch.begin;
+  c.m = P.m + ch.begin;
+  c.v = P.v + ch.begin;
+  c.pb = P.p_bf16 ? P.p_bf16 + ch.begin : nullptr;
+  c.len = ch.len;
+  if (c.len == kChunkElems) {
+    const int wm = div_mode(k.wdiv);
+    if (wm == kMulInv) {
+      if (c.pb) adamw_full<kMulInv, true>(c, k);
+      else adamw_full<kMulInv, false>(c, k);
+    } else {
+      if (c.pb) adamw_full<kIeeeDiv, true>(c, k);
+      else adamw_full<kIeeeDiv, false>(c, k);
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int v = v0 + u * kBlock;
-      if (v < nvec) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          adamw_elem(a[u][h].x, p[u][h].x, m[u][h].x, w[u][h].x, k);
-          adamw_elem(a[u][h].y, p[u][h].y, m[u][h].y, w[u][h].y, k);
-          adamw_elem(a[u][h].z, p[u][h].z, m[u][h].z, w[u][h].z, k);
-          adamw_elem(a[u][h].w, p[u][h].w, m[u][h].w, w[u][h].w, k);
-          *reinterpret_cast<float4*>(pm + 8 * v + 4 * h) = p[u][h];
-          *reinterpret_cast<float4*>(mm + 8 * v + 4 * h) = m[u][h];
-          *reinterpret_cast<float4*>(vm + 8 * v + 4 * h) = w[u][h];
-        }
-        if (pb) {
-          uint4 o;
-          o.x = bf16_bits(p[u][0].x) | (bf16_bits(p[u][0].y) << 16);
-          o.y = bf16_bits(p[u][0].z) | (bf16_bits(p[u][0].w) << 16);
-          o.z = bf16_bits(p[u][1].x) | (bf16_bits(p[u][1].y) << 16);
-          o.w = bf16_bits(p[u][1].z) | (bf16_bits(p[u][1].w) << 16);
-          *reinterpret_cast<uint4*>(pb + 8 * v) = o;
-        }
-      }
-    }
-  }
-  if ((ch.len & 7) && int(threadIdx.x) == nvec % kBlock) {
-    for (int i = nvec * 8; i < ch.len; ++i) {
-      float p1 = pm[i], m1 = mm[i], v1 = vm[i];
-      adamw_elem(acc[i], p1, m1, v1, k);
-      pm[i] = p1;
-      mm[i] = m1;
-      vm[i] = v1;
-      if (pb) pb[i] = uint16_t(bf16_bits(p1));
-    }
+  } else {
+    adamw_generic(c, k);
   }
 }
 

@@ -13,7 +13,10 @@ namespace gro {
 // Elements per chunk.  A chunk is one workgroup's unit of work in every pass
 // and the granularity of the global norm's partial sums, so the norm's
 // summation order is fixed by the plan, never by the launch shape.
-constexpr int32_t kChunkElems = 16384;
+#ifndef GRO_CHUNK_ELEMS
+#define GRO_CHUNK_ELEMS 4096
+#endif
+constexpr int32_t kChunkElems = GRO_CHUNK_ELEMS;
 // Bucket bases and slot strides are multiples of this many elements
 // (256 B of FP32, 128 B of BF16) so every chunk starts 128-bit aligned.
 constexpr int64_t kAlignElems = 64;

@@ -84,7 +84,10 @@ class Case:
         self.m_h: Dict[int, np.ndarray] = {}
         self.v_h: Dict[int, np.ndarray] = {}
         for i, o in enumerate(self.owners):
-            if not o.updated or w.tensors[i].numel == 0:
+            if not o.updated:
+                continue
+            if w.tensors[i].numel == 0:
+                self.master_h[i] = self.m_h[i] = self.v_h[i] = np.zeros(0, np.float32)
                 continue
             p = synth.master_init(w, i, device=device)
             self.st.flat_view(self.st.master, i).copy_(p)
@@ -98,8 +101,11 @@ class Case:
         """Per-tensor per-slot BF16 gradients of microbatch k of step."""
         out = []
         for i, o in enumerate(self.owners):
-            if o.owner == M.EXCLUDED or self.w.tensors[i].numel == 0:
+            if o.owner == M.EXCLUDED:
                 out.append(None)
+                continue
+            if self.w.tensors[i].numel == 0:
+                out.append([torch.zeros(0, dtype=torch.bfloat16, device=self.device)] * o.slots)
                 continue
             out.append([synth.grad_bf16(self.w, i, 1000 * step + k, r, device=self.device)
                         for r in range(o.slots)])

@@ -42,7 +42,8 @@ def ragged_workload(R=2, seed=7, bucket_elems=25_000_000, sizes=None):
     frozen and a no-decay tensor."""
     rng = np.random.default_rng(seed)
     if sizes is None:
-        sizes = [1, 7, 8, 9, 63, 65, 1000, 16383, 16384, 16385, 40000, 70001, 3 * 16384 + 5]
+        sizes = [1, 7, 8, 9, 63, 65, 1000, 4095, 4096, 4097, 8193, 16383, 16384, 16385, 40000, 70001,
+                 3 * 16384 + 5]
     tensors = []
     for i, n in enumerate(sizes):
         pl = synth.PLACEMENTS[i % 4]

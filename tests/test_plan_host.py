@@ -14,7 +14,6 @@ from gradient_reduction_optimizer_amd import synth
 from gradient_reduction_optimizer_amd.buffers import Plan
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CHUNK = 16384
 ALIGN = 64
 
 
@@ -52,6 +51,7 @@ def _check_table(tensors, R, bucket_elems):
 
 def _check_layout(plan, tensors, cap):
     info, buckets = plan.info, plan.buckets
+    CHUNK = info["chunk_elems"]
     # chunks partition each bucket; buckets are disjoint, aligned, ordered
     q = 0
     end = 0
