@@ -135,83 +135,88 @@ def main():
                            st.p_bf16.data_ptr())
     torch.cuda.synchronize()
 
-    ev = {"accumulate": [], "adamw": [], "norm": []}
+    N = info["n_owned"]
+    c_mix = sum(bk["len"] * bk["slots"] for bk in plan.buckets)  # sum over elements of c
+    window_ptrs = [p for k in range(n) for p in grads[k]]       # microbatch-major
     step_no = [0]
 
-    def one_step(record: bool):
-        step_no[0] += 1
-        for k in range(n):
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            B.gro_accumulate(plan.handle, 0, nb, grads[k], acc, k, n, s)
-            if record:
-                e1 = torch.cuda.Event(enable_timing=True)
-                e1.record(stream)
-                ev["accumulate"].append((e0, e1))
-        if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        B.gro_reduce_norm(plan.handle, acc, n, s)
-        if record:
-            e1 = torch.cuda.Event(enable_timing=True)
-            e1.record(stream)
-            ev["norm"].append((e0, e1))
-            e2 = torch.cuda.Event(enable_timing=True)
-            e2.record(stream)
-        B.gro_clip_adamw(plan.handle, acc, n, w.max_norm, w.hparams, step_no[0], mp, mm, vm, pb, s)
-        if record:
-            e3 = torch.cuda.Event(enable_timing=True)
-            e3.record(stream)
-            ev["adamw"].append((e2, e3))
+    def ev_pair():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
 
-    for _ in range(args.warmup):
-        one_step(False)
-    torch.cuda.synchronize()
-    # Timed region: exactly `steps` steps.  HIP events recorded on the launch
-    # stream around each call give the per-kernel durations (a stream marker
-    # costs a few microseconds at most).
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    norm, _, finite = B.gro_plan_get_norm(plan.handle)
-    if not finite:
-        raise RuntimeError("the benchmark's norm is not finite: the timed steps skipped the update")
+    def one_step(mode: str, ev: dict):
+        step_no[0] += 1
+        if mode == "microbatch":
+            for k in range(n):
+                e0 = ev_pair()
+                B.gro_accumulate(plan.handle, 0, nb, grads[k], acc, k, n, s)
+                ev["k_accumulate"].append((e0, ev_pair()))
+        else:
+            e0 = ev_pair()
+            B.gro_accumulate_window(plan.handle, 0, nb, window_ptrs, n, acc, s)
+            ev["k_accumulate_window"].append((e0, ev_pair()))
+        e0 = ev_pair()
+        B.gro_reduce_norm(plan.handle, acc, n, s)
+        ev["k_norm_final"].append((e0, ev_pair()))
+        e0 = ev_pair()
+        B.gro_clip_adamw(plan.handle, acc, n, w.max_norm, w.hparams, step_no[0], mp, mm, vm, pb, s)
+        ev["k_adamw"].append((e0, ev_pair()))
 
     def avg_ms(pairs):
         return sum(a.elapsed_time(b) for a, b in pairs) / max(len(pairs), 1)
 
-    N = info["n_owned"]
-    c_mix = sum(bk["len"] * bk["slots"] for bk in plan.buckets)  # sum of c over elements
-    # algorithmic bytes: accumulate k=0: 2c+4, k>0: 2c+8 per element; AdamW: 30 per element
-    acc_bytes = [2 * c_mix + 4 * N] + [2 * c_mix + 8 * N] * (n - 1)
-    acc_bytes_avg = sum(acc_bytes) / n
-    adam_bytes = 30 * N
-    t_acc = avg_ms(ev["accumulate"])
-    t_adam = avg_ms(ev["adamw"])
-    t_norm = avg_ms(ev["norm"])
-    kernels = {
-        "k_accumulate": {"launches_per_step": n, "avg_ms": t_acc, "alg_bytes_per_launch": acc_bytes_avg,
-                         "GBps": acc_bytes_avg / (t_acc * 1e6)},
-        "k_adamw": {"launches_per_step": 1, "avg_ms": t_adam, "alg_bytes_per_launch": adam_bytes,
-                    "GBps": adam_bytes / (t_adam * 1e6)},
-        "k_norm_final": {"launches_per_step": 1, "avg_ms": t_norm},
-    }
-    dom = "k_accumulate" if t_acc * n >= t_adam else "k_adamw"
-    kd = kernels[dom]
-    achieved = kd["GBps"]
-    step_bytes = sum(acc_bytes) + adam_bytes
+    def time_mode(mode: str) -> dict:
+        """Warm up, then time exactly `steps` steps (wall clock between two
+        device synchronisations); HIP events recorded on the launch stream
+        around every call give the per-kernel durations."""
+        ev = {"k_accumulate": [], "k_accumulate_window": [], "k_norm_final": [], "k_adamw": []}
+        for _ in range(args.warmup):
+            one_step(mode, {k: [] for k in ev})
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            one_step(mode, ev)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        norm, _, finite = B.gro_plan_get_norm(plan.handle)
+        if not finite:
+            raise RuntimeError("the benchmark's norm is not finite: the timed steps skipped the update")
+        # algorithmic bytes per launch
+        if mode == "microbatch":
+            acc_launch = (n * 2 * c_mix + (4 + 8 * (n - 1)) * N) / n  # k=0: 2c+4, k>0: 2c+8 per element
+            acc_name, acc_launches = "k_accumulate", n
+        else:
+            acc_launch = n * 2 * c_mix + 4 * N                         # all n microbatches + one acc write
+            acc_name, acc_launches = "k_accumulate_window", 1
+        kernels = {
+            acc_name: {"launches_per_step": acc_launches, "avg_ms": avg_ms(ev[acc_name]),
+                       "alg_bytes_per_launch": acc_launch},
+            "k_adamw": {"launches_per_step": 1, "avg_ms": avg_ms(ev["k_adamw"]), "alg_bytes_per_launch": 30 * N},
+            "k_norm_final": {"launches_per_step": 1, "avg_ms": avg_ms(ev["k_norm_final"])},
+        }
+        for k in (acc_name, "k_adamw"):
+            kernels[k]["GBps"] = kernels[k]["alg_bytes_per_launch"] / (kernels[k]["avg_ms"] * 1e6)
+        step_bytes = acc_launch * acc_launches + 30 * N
+        dom = max((acc_name, "k_adamw"), key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
+        log(f"{mode}: {ms:.3f} ms/step, " + ", ".join(f"{k} {v['avg_ms'] * 1e3:.1f} us" for k, v in kernels.items()))
+        return {"ms_per_step": ms, "value": N / (ms * 1e-3) / 1e9, "kernels": kernels, "dominant": dom,
+                "step_hbm": {"alg_bytes": step_bytes, "GBps": step_bytes / (ms * 1e6),
+                             "frac": step_bytes / (ms * 1e6) / HBM_PEAK_GBS},
+                "final_norm": norm}
+
+    mb = time_mode("microbatch")
+    wnd = time_mode("window")
+    dom = mb["dominant"]
+    achieved = mb["kernels"][dom]["GBps"]
     out = {
         "metric": "Gparam updates/s (67M BF16 step, 1 GPU)",
-        "value": N / (ms_per_step * 1e-3) / 1e9,
+        "value": mb["value"],
         "unit": "Gparam updates/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": mb["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -219,15 +224,19 @@ def main():
         "data": "synthetic: BF16 grads N(0,1e-2) per microbatch, FP32 master N(0,0.02), seeded",
         "config": {"workload": f"{w.name}: 4 layers hidden 1024, 16384x1024 embedding, "
                                f"{w.numel} params as this GPU's share, R={w.R} stacked TP slots, "
-                               f"accumulation window {n}, clip {w.max_norm}, AdamW",
+                               f"accumulation window {n} (one gro_accumulate per microbatch), "
+                               f"clip {w.max_norm}, AdamW",
                    "params": w.numel, "R": w.R, "window": n, "bucket_elems": w.bucket_elems,
                    "n_buckets": nb, "n_chunks": info["n_chunks"], "parallelism": "single GPU share"},
-        "step_hbm": {"alg_bytes": step_bytes, "GBps": step_bytes / (ms_per_step * 1e6),
-                     "frac": step_bytes / (ms_per_step * 1e6) / HBM_PEAK_GBS},
+        "step_hbm": mb["step_hbm"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dom)},
-        "kernels": kernels,
-        "final_norm": norm,
+        "kernels": mb["kernels"],
+        "final_norm": mb["final_norm"],
+        "window_call": {"note": "same step with one gro_accumulate_window per window (every microbatch's "
+                                "gradient buckets resident); bit-identical results",
+                        "value": wnd["value"], "ms_per_step": wnd["ms_per_step"], "step_hbm": wnd["step_hbm"],
+                        "kernels": wnd["kernels"]},
         "context": {"pages_ms_per_update_67M": [3.255, 2.624], "hardware_of_pages": "not stated"},
     }
     if not args.no_cpu_baseline:

@@ -6,7 +6,7 @@ The library is loaded on first use and there is no fallback: a missing
 library raises.
 """
 from .binding import (  # noqa: F401
-    GroError, gro_accumulate, gro_clip_adamw, gro_last_error, gro_plan_bind, gro_plan_bucket,
+    GroError, gro_accumulate, gro_accumulate_window, gro_clip_adamw, gro_last_error, gro_plan_bind, gro_plan_bucket,
     gro_plan_create, gro_plan_destroy, gro_plan_get_info, gro_plan_get_norm, gro_plan_tensor,
     gro_reduce_norm, load,
 )

@@ -33,8 +33,8 @@ OWNER_NAMES = ("mean", "sum", "local_shard", "local_reduced", "excluded")
 GRO_MAX_NDIM = 8
 
 EXPORTS = ("gro_plan_create", "gro_plan_destroy", "gro_plan_get_info", "gro_plan_tensor",
-           "gro_plan_bucket", "gro_plan_bind", "gro_accumulate", "gro_reduce_norm",
-           "gro_plan_get_norm", "gro_clip_adamw", "gro_last_error")
+           "gro_plan_bucket", "gro_plan_bind", "gro_accumulate", "gro_accumulate_window",
+           "gro_reduce_norm", "gro_plan_get_norm", "gro_clip_adamw", "gro_last_error")
 
 
 class gro_tensor_desc(ctypes.Structure):
@@ -97,6 +97,7 @@ def load() -> ctypes.CDLL:
     L.gro_plan_bucket.argtypes = [P, I32, ctypes.POINTER(gro_bucket_info)]
     L.gro_plan_bind.argtypes = [P, P, U64, P]
     L.gro_accumulate.argtypes = [P, I32, I32, ctypes.POINTER(P), P, I32, I32, P]
+    L.gro_accumulate_window.argtypes = [P, I32, I32, ctypes.POINTER(P), I32, P, P]
     L.gro_reduce_norm.argtypes = [P, P, I32, P]
     L.gro_plan_get_norm.argtypes = [P, ctypes.POINTER(D), ctypes.POINTER(D), ctypes.POINTER(I32)]
     L.gro_clip_adamw.argtypes = [P, P, I32, D, ctypes.POINTER(gro_adamw_hparams), I64, P, P, P, P, P]
@@ -186,6 +187,15 @@ def gro_accumulate(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[int], d
     ptrs = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
     _check(load().gro_accumulate(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, ctypes.c_void_p(d_acc),
                                  int(micro_index), int(window_size), ctypes.c_void_p(stream)))
+
+
+def gro_accumulate_window(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[int], n: int, d_acc: int,
+                          stream: int = 0) -> None:
+    """d_grad_buckets: n*(b1-b0) pointers, microbatch-major."""
+    m = max(len(d_grad_buckets), 1)
+    ptrs = (ctypes.c_void_p * m)(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
+    _check(load().gro_accumulate_window(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, int(n),
+                                        ctypes.c_void_p(d_acc), ctypes.c_void_p(stream)))
 
 
 def gro_reduce_norm(plan: int, d_acc: int, window_size: int, stream: int = 0) -> None:

@@ -140,6 +140,62 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
   return GRO_OK;
 }
 
+extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
+                                     int32_t n, float* d_acc, void* stream) {
+  clear_error();
+  int rc = check_bound(p);
+  if (rc != GRO_OK) return rc;
+  const int32_t nb = int32_t(p->buckets.size());
+  if (b0 < 0 || b1 < b0 || b1 > nb)
+    return set_error(GRO_E_INVALID, "bucket range [%d, %d) not within [0, %d)", b0, b1, nb);
+  if (n < 1) return set_error(GRO_E_INVALID, "a window has at least one microbatch (n = %d)", n);
+  if (n > kMaxBucketsPerLaunch)
+    return set_error(GRO_E_INVALID, "window of %d microbatches exceeds %d", n, kMaxBucketsPerLaunch);
+  if (b1 == b0) return GRO_OK;
+  if (d_grad_buckets == nullptr) return set_error(GRO_E_INVALID, "d_grad_buckets is NULL");
+  if (d_acc == nullptr || !aligned16(d_acc))
+    return set_error(GRO_E_INVALID, "d_acc must be a non-NULL 16-byte aligned device pointer");
+  const int32_t span = b1 - b0;
+  for (int32_t k = 0; k < n; ++k)
+    for (int32_t j = 0; j < span; ++j) {
+      const void* g = d_grad_buckets[int64_t(k) * span + j];
+      if (g == nullptr || !aligned16(g))
+        return set_error(GRO_E_INVALID, "microbatch %d buffer of bucket %d is NULL or not 16-byte aligned",
+                         k, b0 + j);
+    }
+  // Buckets of one launch: n * buckets <= kMaxBucketsPerLaunch pointers.
+  const int32_t per = kMaxBucketsPerLaunch / n;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t lb = b0; lb < b1; lb += per) {
+    const int32_t le = (b1 - lb) < per ? b1 : lb + per;
+    WindowLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.chunks = dev_chunks(p);
+    a.buckets = dev_buckets(p);
+    a.q_begin = p->buckets[size_t(lb)].first_chunk;
+    a.q_end = p->buckets[size_t(le - 1)].first_chunk + p->buckets[size_t(le - 1)].n_chunks;
+    a.b_first = lb;
+    a.n_buckets = le - lb;
+    a.n_micro = n;
+    a.R = p->R;
+    for (int32_t k = 0; k < n; ++k)
+      for (int32_t b = lb; b < le; ++b)
+        a.grads[k * (le - lb) + (b - lb)] =
+            static_cast<const uint16_t*>(d_grad_buckets[int64_t(k) * span + (b - b0)]);
+    a.acc = d_acc;
+    a.partials = dev_partials(p);
+    const hipError_t e = launch_accumulate_window(a, s);
+    if (e != hipSuccess) return hip_fail(e, "accumulate-window launch");
+  }
+  for (int32_t b = b0; b < b1; ++b) {
+    p->count[size_t(b)] = n;
+    p->partials_ready[size_t(b)] = 1;
+  }
+  p->acc_ptr = d_acc;
+  p->norm_done = false;
+  return GRO_OK;
+}
+
 extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_size, void* stream) {
   clear_error();
   int rc = check_bound(p);

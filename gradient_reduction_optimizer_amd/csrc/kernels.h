@@ -27,6 +27,21 @@ struct AccumulateLaunch {
   int32_t window;           // microbatches in the window (used when fuse_norm)
 };
 
+// A whole accumulation window in one pass: grads[k * n_buckets + j] is
+// microbatch k's buffer of bucket b_first + j, n_micro * n_buckets <= 64.
+struct WindowLaunch {
+  const ChunkDev* chunks;
+  const BucketDev* buckets;
+  int64_t q_begin, q_end;
+  int32_t b_first;
+  int32_t n_buckets;
+  int32_t n_micro;
+  int32_t R;
+  const uint16_t* grads[kMaxBucketsPerLaunch];
+  float* acc;
+  double* partials;
+};
+
 struct NormLaunch {
   const ChunkDev* chunks;
   const float* acc;
@@ -53,6 +68,7 @@ struct AdamWLaunch {
 };
 
 hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s);
+hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s);
 hipError_t launch_norm_partials(const NormLaunch& a, hipStream_t s);
 hipError_t launch_norm_final(const double* partials, int64_t n_chunks, double* scalars,
                              hipStream_t s);

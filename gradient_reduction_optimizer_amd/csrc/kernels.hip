@@ -324,6 +324,158 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
   }
 }
 
+// ------------------------------------------------- accumulate a window
+// The whole window in one pass: for every element, the n microbatches'
+// reductions are accumulated in registers in microbatch order (acc = red_0,
+// then acc = acc + red_k) -- the same operations as n accumulate passes --
+// and the accumulator is written once, with the norm partial.
+struct WinChunk {
+  const WindowLaunch* P;
+  int64_t off;         // chunk offset inside its bucket
+  int64_t stride;
+  int j;               // bucket index within the launch
+  float* acc;
+  int len;
+  int slots;
+  bool mean;
+  Divisor rdiv;
+  Divisor wdiv;
+  __device__ const uint16_t* g(int k) const { return P->grads[k * P->n_buckets + j] + off; }
+};
+
+__device__ __forceinline__ float win_reduce1(const WinChunk& c, int k, int i) {
+  const uint16_t* g = c.g(k);
+  float s = widen1(g[i]);
+  for (int r = 1; r < c.slots; ++r) s = s + widen1(g[int64_t(r) * c.stride + i]);
+  return c.mean ? divide(s, c.rdiv) : s;
+}
+
+// Any chunk, any slot count: runtime checks, same order.
+__device__ double window_generic(const WinChunk& c) {
+  const int n = c.P->n_micro;
+  const int nvec = c.len >> 2;
+  double ss = 0.0;
+  for (int v = threadIdx.x; v < nvec; v += kBlock) {
+    f32x4 acc;
+    for (int k = 0; k < n; ++k) {
+      const uint16_t* g = c.g(k);
+      f32x4 red = widen4(ld2u(g + 4 * v));
+      for (int r = 1; r < c.slots; ++r) red = red + widen4(ld2u(g + int64_t(r) * c.stride + 4 * v));
+      if (c.mean) {
+        red.x = divide(red.x, c.rdiv);
+        red.y = divide(red.y, c.rdiv);
+        red.z = divide(red.z, c.rdiv);
+        red.w = divide(red.w, c.rdiv);
+      }
+      acc = k == 0 ? red : acc + red;
+    }
+    st4f(c.acc + 4 * v, acc);
+    ss += sq(divide(acc.x, c.wdiv));
+    ss += sq(divide(acc.y, c.wdiv));
+    ss += sq(divide(acc.z, c.wdiv));
+    ss += sq(divide(acc.w, c.wdiv));
+  }
+  if ((c.len & 3) && int(threadIdx.x) == nvec % kBlock) {
+    for (int i = nvec * 4; i < c.len; ++i) {
+      float a = win_reduce1(c, 0, i);
+      for (int k = 1; k < n; ++k) a = a + win_reduce1(c, k, i);
+      c.acc[i] = a;
+      ss += sq(divide(a, c.wdiv));
+    }
+  }
+  return ss;
+}
+
+// A full chunk with C slots, the MEAN divisor mode RM and the window
+// divisor mode WM fixed at compile time.  Microbatch k+1's loads are issued
+// before microbatch k's data is consumed.
+template <int C, int RM, int WM>
+__device__ double window_full(const WinChunk& c) {
+  constexpr int nvec = kChunkElems / 4;
+  const int n = c.P->n_micro;
+  double ss = 0.0;
+#pragma unroll 1
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    f32x4 acc[kUnroll];
+    u32x2 cur[kUnroll][C], nxt[kUnroll][C];
+    {
+      const uint16_t* g = c.g(0);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int r = 0; r < C; ++r) cur[u][r] = ld2u(g + int64_t(r) * c.stride + 4 * (v0 + u * kBlock));
+    }
+#pragma unroll 1
+    for (int k = 0; k < n; ++k) {
+      if (k + 1 < n) {
+        const uint16_t* g = c.g(k + 1);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int r = 0; r < C; ++r) nxt[u][r] = ld2u(g + int64_t(r) * c.stride + 4 * (v0 + u * kBlock));
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        f32x4 red = widen4(cur[u][0]);
+#pragma unroll
+        for (int r = 1; r < C; ++r) red = red + widen4(cur[u][r]);
+        red.x = divide_m<RM>(red.x, c.rdiv);
+        red.y = divide_m<RM>(red.y, c.rdiv);
+        red.z = divide_m<RM>(red.z, c.rdiv);
+        red.w = divide_m<RM>(red.w, c.rdiv);
+        acc[u] = k == 0 ? red : acc[u] + red;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int r = 0; r < C; ++r) cur[u][r] = nxt[u][r];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      st4f(c.acc + 4 * (v0 + u * kBlock), acc[u]);
+      ss += sq(divide_m<WM>(acc[u].x, c.wdiv));
+      ss += sq(divide_m<WM>(acc[u].y, c.wdiv));
+      ss += sq(divide_m<WM>(acc[u].z, c.wdiv));
+      ss += sq(divide_m<WM>(acc[u].w, c.wdiv));
+    }
+  }
+  return ss;
+}
+
+template <int C, int RM>
+__device__ double window_full_dispatch(const WinChunk& c) {
+  return c.wdiv.pow2 ? window_full<C, RM, kMulInv>(c) : window_full<C, RM, kIeeeDiv>(c);
+}
+
+__global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch P) {
+  const int64_t q = chunk_of_block(P.q_begin);
+  if (q < P.q_begin || q >= P.q_end) return;
+  const ChunkDev ch = P.chunks[q];
+  const BucketDev bk = P.buckets[ch.bucket];
+  WinChunk c;
+  c.P = &P;
+  c.off = ch.begin - bk.base;
+  c.stride = bk.stride;
+  c.j = ch.bucket - P.b_first;
+  c.acc = P.acc + ch.begin;
+  c.len = ch.len;
+  c.slots = bk.slots;
+  c.mean = bk.owner == GRO_OWNER_MEAN;
+  c.rdiv = make_divisor(P.R);
+  c.wdiv = make_divisor(P.n_micro);
+  double ss;
+  if (c.len == kChunkElems && c.slots == 1 && !c.mean)
+    ss = window_full_dispatch<1, kNoDiv>(c);
+  else if (c.len == kChunkElems && c.slots == 2 && !c.mean)
+    ss = window_full_dispatch<2, kNoDiv>(c);
+  else if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2)
+    ss = window_full_dispatch<2, kMulInv>(c);
+  else
+    ss = window_generic(c);
+  const double t = block_sum(ss);
+  if (threadIdx.x == 0) P.partials[q] = t;
+}
+
 // ------------------------------------------------------- norm, stage 1
 // Lane's sum of (acc/window)^2 over its vectors of a full chunk.
 template <int WM>
@@ -396,8 +548,18 @@ __global__ __launch_bounds__(kBlock) void k_norm_partials(const NormLaunch P) {
 // butterfly and the sixteen wave totals in order.  No atomics.
 __global__ __launch_bounds__(kFinalBlock) void k_norm_final(const double* __restrict__ partials,
                                                             int64_t n, double* __restrict__ scalars) {
+  // Lane t adds partials t, t+1024, t+2048, ... in that order; the loads of
+  // eight consecutive terms are issued together so they overlap.
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += kFinalBlock) s += partials[i];
+  int64_t i = threadIdx.x;
+  for (; i + 7 * kFinalBlock < n; i += 8 * kFinalBlock) {
+    double x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = partials[i + j * kFinalBlock];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += x[j];
+  }
+  for (; i < n; i += kFinalBlock) s += partials[i];
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
   __shared__ double part[kFinalBlock / 64];
@@ -575,6 +737,13 @@ hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
   const int64_t blocks = (a.q_end - a.q_begin) + (a.q_begin & 7);
   hipLaunchKernelGGL(k_accumulate, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s) {
+  if (a.q_end <= a.q_begin) return hipSuccess;
+  const int64_t blocks = (a.q_end - a.q_begin) + (a.q_begin & 7);
+  hipLaunchKernelGGL(k_accumulate_window, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -190,6 +190,21 @@ int gro_plan_bind(gro_plan* plan, void* d_workspace, uint64_t bytes, void* strea
 int gro_accumulate(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
                    float* d_acc, int32_t micro_index, int32_t window_size, void* stream);
 
+/* The whole window of n microbatches for buckets [b0, b1) in one pass:
+ * bit for bit what gro_accumulate with micro_index 0..n-1 and window_size n
+ * computes (per element: acc = red_0, then acc = acc + red_k in microbatch
+ * order; norm partials written at the end), but the accumulator is written
+ * once instead of being read and written n times.  For callers that keep
+ * every microbatch's gradient buckets resident until the window ends (on a
+ * 288 GB MI355X this trades n * sum_b(slots_b * slot_stride_b) BF16
+ * elements of memory for (8n - 4) bytes per element less traffic).
+ * d_grad_buckets: host array of n*(b1-b0) device pointers, microbatch-major:
+ * entry k*(b1-b0) + j is microbatch k's BF16 buffer [slots][slot_stride] of
+ * bucket b0+j.  n >= 1.  Leaves these buckets with a complete window of n
+ * (any earlier partial window of theirs is discarded). */
+int gro_accumulate_window(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
+                          int32_t n, float* d_acc, void* stream);
+
 /* Global L2 norm of g = acc / window_size over every owned element, in FP64,
  * with no atomics: per-chunk partials summed in a fixed order, so the result
  * does not depend on launch shape and is bit-reproducible.  Every bucket must

@@ -95,6 +95,7 @@ class Case:
             self.m_h[i] = np.zeros(w.tensors[i].numel, np.float32)
             self.v_h[i] = np.zeros(w.tensors[i].numel, np.float32)
         self.bufs = self.st.grad_buffers()
+        self.window_bufs = []
         torch.cuda.synchronize()
 
     def draw(self, step: int, k: int):
@@ -125,6 +126,19 @@ class Case:
             for b in bucket_order:
                 B.gro_accumulate(self.plan.handle, b, b + 1, [ptrs[b]], self.st.acc.data_ptr(), k,
                                  n if fuse else 0, self.stream)
+
+    def gpu_accumulate_window(self, grads_per_micro, n: int):
+        """Pack each microbatch into its own bucket-buffer set, then reduce and
+        accumulate the whole window in one call."""
+        while len(self.window_bufs) < n:
+            self.window_bufs.append(self.st.grad_buffers())
+        for k in range(n):
+            for i, g in enumerate(grads_per_micro[k]):
+                if g is not None:
+                    self.st.pack(self.window_bufs[k], i, g)
+        nb = self.plan.info["n_buckets"]
+        ptrs = [self.window_bufs[k][b].data_ptr() for k in range(n) for b in range(nb)]
+        B.gro_accumulate_window(self.plan.handle, 0, nb, ptrs, n, self.st.acc.data_ptr(), self.stream)
 
     def gpu_finish(self, n: int, step: int, max_norm: float, with_bf16=True):
         B.gro_reduce_norm(self.plan.handle, self.st.acc.data_ptr(), n, self.stream)
@@ -162,18 +176,27 @@ class Case:
 
 
 def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[float] = None,
-               fuse: bool = True, R: Optional[int] = None, bucket_order=None, log=print):
-    """Run len(windows) optimizer steps on both sides and compare after each."""
+               fuse: bool = True, R: Optional[int] = None, bucket_order=None, window_call: bool = False,
+               log=print):
+    """Run len(windows) optimizer steps on both sides and compare after each.
+    window_call: use gro_accumulate_window (one call per window) instead of
+    one gro_accumulate per microbatch."""
     c = Case(w, R=R)
     max_norm = w.max_norm if max_norm is None else max_norm
     cmps = {k: Compare(k) for k in ("acc", "master", "m", "v", "p_bf16")}
     norms = []
     for step, n in enumerate(windows, start=1):
         grads_host = []
+        micro = []
         for k in range(n):
             g = c.draw(step, k)
-            c.gpu_accumulate(g, k, n, fuse=fuse, bucket_order=bucket_order)
+            if window_call:
+                micro.append(g)
+            else:
+                c.gpu_accumulate(g, k, n, fuse=fuse, bucket_order=bucket_order)
             grads_host.append([None if x is None else [bits16(s) for s in x] for x in g])
+        if window_call:
+            c.gpu_accumulate_window(micro, n)
         norm, norm_sq, finite = c.gpu_finish(n, step, max_norm)
         res = c.oracle_window(grads_host, step, max_norm)
         c.compare_acc(res, cmps["acc"])

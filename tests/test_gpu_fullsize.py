@@ -51,3 +51,14 @@ def test_full_size_parity(name):
     log(f"case {name} done in {time.time() - t0:.1f} s, {c.plan.info['n_buckets']} buckets, "
         f"{c.plan.info['n_chunks']} chunks")
     assert_parity(cmps, norms)
+
+
+@pytest.mark.parametrize("name", ["draft-67m", "dense-1b-fsdp8-shard"])
+def test_full_size_parity_window_call(name):
+    """The one-call-per-window entry point at full size."""
+    w = CASES[name]()
+    t0 = time.time()
+    log(f"case {name} (window call): {w.numel} elements, windows {w.windows}")
+    c, cmps, norms = run_parity(w, w.windows, window_call=True, log=log)
+    log(f"case {name} (window call) done in {time.time() - t0:.1f} s")
+    assert_parity(cmps, norms)

@@ -115,6 +115,31 @@ def test_unfused_and_per_bucket_calls_give_identical_bits():
     assert [n[0] for n in na] == [n[0] for n in nb_] == [n[0] for n in nc]
 
 
+@pytest.mark.parametrize("R", [1, 2, 3])
+def test_window_call_matches_oracle_and_microbatch_calls(R):
+    """gro_accumulate_window gives the oracle's results and the same bits as
+    one gro_accumulate per microbatch, for full, trailing and single windows."""
+    w = ragged_workload(R=R, bucket_elems=30000)
+    log(f"case window call R={R}")
+    ca, cmps, na = run_parity(w, [3, 4, 1, 8], window_call=True, log=log)
+    assert_parity(cmps, na)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+    cb, _, nb_ = run_parity(w, [3, 4, 1, 8], window_call=False, log=log)
+    for arr in ("acc", "master", "m", "v"):
+        assert torch.equal(getattr(ca.st, arr).view(torch.int32), getattr(cb.st, arr).view(torch.int32)), arr
+    assert [n[0] for n in na] == [n[0] for n in nb_]
+
+
+def test_window_call_tiny_and_many_buckets():
+    for w in (synth.tiny(), synth.tiny(bucket_elems=4096)):
+        log(f"case window call {w.name} cap={w.bucket_elems}")
+        c, cmps, norms = run_parity(w, [2, 5], window_call=True, log=log)
+        assert_parity(cmps, norms)
+        for k in cmps.values():
+            assert k.n_diff_bits == 0, str(k)
+
+
 @pytest.mark.parametrize("max_norm", [0.0, float("inf"), -1.0, 1e-3, 1e9])
 def test_clip_settings(max_norm):
     w = synth.tiny()
