@@ -442,9 +442,61 @@ __device__ double window_full(const WinChunk& c) {
   return ss;
 }
 
+// Common window lengths: every microbatch's loads are issued before any
+// is consumed (N * C * kUnroll loads in flight per lane).
+template <int C, int RM, int WM, int N>
+__device__ double window_full_n(const WinChunk& c) {
+  constexpr int nvec = kChunkElems / 4;
+  double ss = 0.0;
+#pragma unroll 1
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
+    u32x2 raw[N][kUnroll][C];
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint16_t* g = c.g(k);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int r = 0; r < C; ++r) raw[k][u][r] = ld2u(g + int64_t(r) * c.stride + 4 * (v0 + u * kBlock));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      f32x4 acc;
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        f32x4 red = widen4(raw[k][u][0]);
+#pragma unroll
+        for (int r = 1; r < C; ++r) red = red + widen4(raw[k][u][r]);
+        red.x = divide_m<RM>(red.x, c.rdiv);
+        red.y = divide_m<RM>(red.y, c.rdiv);
+        red.z = divide_m<RM>(red.z, c.rdiv);
+        red.w = divide_m<RM>(red.w, c.rdiv);
+        acc = k == 0 ? red : acc + red;
+      }
+      st4f(c.acc + 4 * (v0 + u * kBlock), acc);
+      ss += sq(divide_m<WM>(acc.x, c.wdiv));
+      ss += sq(divide_m<WM>(acc.y, c.wdiv));
+      ss += sq(divide_m<WM>(acc.z, c.wdiv));
+      ss += sq(divide_m<WM>(acc.w, c.wdiv));
+    }
+  }
+  return ss;
+}
+
+template <int C, int RM, int WM>
+__device__ double window_full_w(const WinChunk& c) {
+  switch (c.P->n_micro) {
+    case 2: return window_full_n<C, RM, WM, 2>(c);
+    case 3: return window_full_n<C, RM, WM, 3>(c);
+    case 4: return window_full_n<C, RM, WM, 4>(c);
+    case 8: return window_full_n<C, RM, WM, 8>(c);
+    default: return window_full<C, RM, WM>(c);
+  }
+}
+
 template <int C, int RM>
 __device__ double window_full_dispatch(const WinChunk& c) {
-  return c.wdiv.pow2 ? window_full<C, RM, kMulInv>(c) : window_full<C, RM, kIeeeDiv>(c);
+  return c.wdiv.pow2 ? window_full_w<C, RM, kMulInv>(c) : window_full_w<C, RM, kIeeeDiv>(c);
 }
 
 __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch P) {
@@ -687,8 +739,11 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
   }
 }
 
+// Chunks are visited last to first: the step's last accumulate pass has just
+// written the accumulator front to back, so its final stretch is still in
+// the MI355X's memory-side Infinity Cache when this pass starts.
 __global__ __launch_bounds__(kBlock) void k_adamw(const AdamWLaunch P) {
-  const int64_t q = int64_t(blockIdx.x);
+  const int64_t q = P.n_chunks - 1 - int64_t(blockIdx.x);
   if (q >= P.n_chunks) return;
   if (P.scalars[kFinite] == 0.0) return;  // non-finite norm: skip the step
   AdamScalars k;

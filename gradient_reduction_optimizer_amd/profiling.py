@@ -18,13 +18,13 @@ import os
 import sys
 from collections import defaultdict
 
-OURS = ("k_accumulate", "k_adamw", "k_norm_partials", "k_norm_final")
+OURS = ("k_accumulate_window", "k_accumulate", "k_adamw", "k_norm_partials", "k_norm_final")
 KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "kernels.hip")
 
 
 def short_name(name: str) -> str:
-    for k in OURS:
-        if k in name:
+    for k in OURS:  # longest names first
+        if k + "(" in name or name.endswith(k) or f"::{k}" in name:
             return k
     if "copyBuffer" in name or "copy" in name.lower():
         return "copy"
