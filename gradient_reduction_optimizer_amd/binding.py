@@ -27,7 +27,8 @@ ERROR_NAMES = {GRO_E_INVALID: "invalid", GRO_E_PLACEMENT: "placement",
 GRO_REPLICATE, GRO_PARTIAL, GRO_SHARD, GRO_REDUCED = 0, 1, 2, 3
 PLACEMENT_CODES = {"replicate": GRO_REPLICATE, "partial": GRO_PARTIAL,
                    "shard": GRO_SHARD, "reduced": GRO_REDUCED}
-GRO_NO_DECAY, GRO_FROZEN = 1, 2
+GRO_NO_DECAY, GRO_FROZEN, GRO_FP32_GRAD = 1, 2, 4
+GRO_GRAD_BF16, GRO_GRAD_FP32 = 0, 1
 GRO_OWNER_MEAN, GRO_OWNER_SUM, GRO_OWNER_LOCAL_SHARD, GRO_OWNER_LOCAL_REDUCED, GRO_OWNER_EXCLUDED = range(5)
 OWNER_NAMES = ("mean", "sum", "local_shard", "local_reduced", "excluded")
 GRO_MAX_NDIM = 8
@@ -55,14 +56,14 @@ class gro_tensor_layout(ctypes.Structure):
                 ("owner", ctypes.c_int32), ("slots", ctypes.c_int32), ("divisor", ctypes.c_int32),
                 ("in_norm", ctypes.c_int32), ("updated", ctypes.c_int32), ("decayed", ctypes.c_int32),
                 ("first_bucket", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("grad_dtype", ctypes.c_int32)]
 
 
 class gro_bucket_info(ctypes.Structure):
     _fields_ = [("flat_base", ctypes.c_int64), ("len", ctypes.c_int64), ("slot_stride", ctypes.c_int64),
                 ("first_chunk", ctypes.c_int64), ("n_chunks", ctypes.c_int64),
                 ("owner", ctypes.c_int32), ("slots", ctypes.c_int32), ("decayed", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("grad_dtype", ctypes.c_int32)]
 
 
 class gro_adamw_hparams(ctypes.Structure):
@@ -128,7 +129,7 @@ def _attr(t, name, default=None):
 def gro_plan_create(tensors: Sequence, R: int, bucket_elems: int) -> int:
     """``tensors``: objects or dicts with param_id, shape, placement (a
     GRO_* code or "replicate"/"partial"/"shard"/"reduced"), shard_index,
-    and optional frozen / no_decay.  Returns the plan handle (an int)."""
+    and optional frozen / no_decay / fp32_grad.  Returns the plan handle."""
     n = len(tensors)
     descs = (gro_tensor_desc * max(n, 1))()
     keep = []
@@ -141,7 +142,8 @@ def gro_plan_create(tensors: Sequence, R: int, bucket_elems: int) -> int:
         if isinstance(pl, str):
             pl = 99  # unknown name: let the library reject it
         flags = (GRO_FROZEN if _attr(t, "frozen", False) else 0) | \
-                (GRO_NO_DECAY if _attr(t, "no_decay", False) else 0) | int(_attr(t, "flags", 0) or 0)
+                (GRO_NO_DECAY if _attr(t, "no_decay", False) else 0) | \
+                (GRO_FP32_GRAD if _attr(t, "fp32_grad", False) else 0) | int(_attr(t, "flags", 0) or 0)
         descs[i] = gro_tensor_desc(int(_attr(t, "param_id")), ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)),
                                    len(shape), int(pl), int(_attr(t, "shard_index", -1)), flags)
     out = ctypes.c_void_p()
@@ -155,7 +157,7 @@ def gro_plan_destroy(plan: int) -> None:
 
 
 def _struct_dict(s) -> dict:
-    return {name: getattr(s, name) for name, _ in s._fields_ if name != "reserved"}
+    return {name: getattr(s, name) for name, _ in s._fields_}
 
 
 def gro_plan_get_info(plan: int) -> dict:

@@ -71,15 +71,18 @@ class DeviceState:
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         B.gro_plan_bind(plan.handle, self.ws_ptr, nbytes, self.stream.cuda_stream)
 
-    def grad_buffers(self, fill=None) -> List:
-        """One BF16 [slots, slot_stride] buffer per bucket (zeros)."""
+    def grad_buffers(self) -> List:
+        """One [slots, slot_stride] buffer per bucket (zeros), BF16 or FP32
+        as the bucket's gradient type says."""
         import torch
-        return [torch.zeros((bk["slots"], bk["slot_stride"]), dtype=torch.bfloat16, device=self.device)
+        return [torch.zeros((bk["slots"], bk["slot_stride"]),
+                            dtype=torch.float32 if bk["grad_dtype"] == B.GRO_GRAD_FP32 else torch.bfloat16,
+                            device=self.device)
                 for bk in self.plan.buckets]
 
     def pack(self, bufs: List, i: int, slot_grads: Sequence) -> None:
-        """Copy tensor i's per-slot BF16 gradients (1-D, length numel) into
-        the bucket buffers."""
+        """Copy tensor i's per-slot gradients (1-D, length numel, the
+        bucket's type) into the bucket buffers."""
         for b, dst, src, cnt in self.plan.segments(i):
             for r, g in enumerate(slot_grads):
                 bufs[b][r, dst:dst + cnt].copy_(g[src:src + cnt], non_blocking=True)

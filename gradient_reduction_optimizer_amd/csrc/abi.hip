@@ -121,7 +121,7 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
     a.q_end = p->buckets[size_t(le - 1)].first_chunk + p->buckets[size_t(le - 1)].n_chunks;
     a.b_first = lb;
     a.n_grads = le - lb;
-    for (int32_t b = lb; b < le; ++b) a.grads[b - lb] = static_cast<const uint16_t*>(d_grad_buckets[b - b0]);
+    for (int32_t b = lb; b < le; ++b) a.grads[b - lb] = d_grad_buckets[b - b0];
     a.acc = d_acc;
     a.partials = dev_partials(p);
     a.R = p->R;
@@ -180,8 +180,7 @@ extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const 
     a.R = p->R;
     for (int32_t k = 0; k < n; ++k)
       for (int32_t b = lb; b < le; ++b)
-        a.grads[k * (le - lb) + (b - lb)] =
-            static_cast<const uint16_t*>(d_grad_buckets[int64_t(k) * span + (b - b0)]);
+        a.grads[k * (le - lb) + (b - lb)] = d_grad_buckets[int64_t(k) * span + (b - b0)];
     a.acc = d_acc;
     a.partials = dev_partials(p);
     const hipError_t e = launch_accumulate_window(a, s);

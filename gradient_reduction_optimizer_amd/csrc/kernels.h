@@ -18,7 +18,7 @@ struct AccumulateLaunch {
   int64_t q_begin, q_end;   // chunk range [q_begin, q_end)
   int32_t b_first;          // bucket index of grads[0]
   int32_t n_grads;
-  const uint16_t* grads[kMaxBucketsPerLaunch];
+  const void* grads[kMaxBucketsPerLaunch];  // BF16 or FP32 per bucket
   float* acc;
   double* partials;         // norm partials (written only when fuse_norm)
   int32_t R;
@@ -37,7 +37,7 @@ struct WindowLaunch {
   int32_t n_buckets;
   int32_t n_micro;
   int32_t R;
-  const uint16_t* grads[kMaxBucketsPerLaunch];
+  const void* grads[kMaxBucketsPerLaunch];
   float* acc;
   double* partials;
 };

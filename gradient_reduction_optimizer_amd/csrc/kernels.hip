@@ -42,7 +42,14 @@ namespace {
 
 constexpr int kBlock = GRO_BLOCK;      // lanes per workgroup (waves of 64)
 constexpr int kWaves = kBlock / 64;
+#ifndef GRO_UNROLL_ADAMW
+#define GRO_UNROLL_ADAMW GRO_UNROLL
+#endif
+#ifndef GRO_ADAMW_MIN_BLOCKS
+#define GRO_ADAMW_MIN_BLOCKS 1
+#endif
 constexpr int kUnroll = GRO_UNROLL;    // 4-element vectors in flight per lane
+constexpr int kUnrollAdam = GRO_UNROLL_ADAMW;
 constexpr int kFinalBlock = 1024;      // the norm's second stage
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
 static_assert(kChunkElems % (4 * kBlock) == 0, "chunks are whole workgroup tiles");
@@ -136,9 +143,34 @@ __device__ __forceinline__ double sq(float x) {
   return d * d;
 }
 
+// ------------------------------------------------------ gradient inputs
+// A bucket's gradient contributions are BF16 (widened exactly) or FP32 (used
+// as they are); the element type is a template parameter of every path.
+struct Bf16In {
+  typedef u32x2 raw_t;
+  static __device__ __forceinline__ raw_t load(const void* base, int64_t e) {
+    return ld2u(static_cast<const uint16_t*>(base) + e);
+  }
+  static __device__ __forceinline__ f32x4 widen(const raw_t r) { return widen4(r); }
+  static __device__ __forceinline__ float load1(const void* base, int64_t i) {
+    return widen1(static_cast<const uint16_t*>(base)[i]);
+  }
+};
+struct F32In {
+  typedef f32x4 raw_t;
+  static __device__ __forceinline__ raw_t load(const void* base, int64_t e) {
+    return ld4f(static_cast<const float*>(base) + e);
+  }
+  static __device__ __forceinline__ f32x4 widen(const raw_t r) { return r; }
+  static __device__ __forceinline__ float load1(const void* base, int64_t i) {
+    return static_cast<const float*>(base)[i];
+  }
+};
+
 // ------------------------------------------------------------ accumulate
 struct AccChunk {
-  const uint16_t* g;   // slot 0 of this chunk in the bucket's gradient buffer
+  const void* g;       // the bucket's gradient buffer [slots][stride]
+  int64_t off;         // this chunk's first element inside the bucket
   int64_t stride;      // slot stride (elements)
   float* acc;          // this chunk in the flat accumulator
   int len;
@@ -151,20 +183,22 @@ struct AccChunk {
 };
 
 // One element's reduction: slots summed in slot order, then /R for MEAN.
-// (The vector path below performs exactly these operations lane-wise.)
+// (The vector paths perform exactly these operations lane-wise.)
+template <typename In>
 __device__ __forceinline__ float reduce1(const AccChunk& c, int i) {
-  float s = widen1(c.g[i]);
-  for (int r = 1; r < c.slots; ++r) s = s + widen1(c.g[int64_t(r) * c.stride + i]);
+  float s = In::load1(c.g, c.off + i);
+  for (int r = 1; r < c.slots; ++r) s = s + In::load1(c.g, int64_t(r) * c.stride + c.off + i);
   return c.mean ? divide(s, c.rdiv) : s;
 }
 
 // Ragged tail [4*nvec, len): handled by the lane that owns vector nvec, after
 // its full vectors, so the lane's element order stays ascending.
+template <typename In>
 __device__ __forceinline__ double accumulate_tail(const AccChunk& c, int nvec) {
   double ss = 0.0;
   if ((c.len & 3) && int(threadIdx.x) == nvec % kBlock) {
     for (int i = nvec * 4; i < c.len; ++i) {
-      float s = reduce1(c, i);
+      float s = reduce1<In>(c, i);
       if (!c.first) s = c.acc[i] + s;
       c.acc[i] = s;
       if (c.fuse) ss += sq(divide(s, c.wdiv));
@@ -177,31 +211,21 @@ __device__ __forceinline__ double accumulate_tail(const AccChunk& c, int nvec) {
 // MEAN, then start or extend the accumulator.  Returns this lane's FP64 sum
 // of (acc/window)^2 over its elements (0 unless fuse), in the lane's element
 // order: its vectors in ascending order, each vector's elements in order,
-// then the tail.  C = slot count known at compile time (0 = runtime).
-template <int C>
+// then the tail.  Any chunk length and slot count; runtime choices.
+template <typename In>
 __device__ double accumulate_generic(const AccChunk& c) {
-  constexpr int kC = C > 0 ? C : 1;
   const int nvec = c.len >> 2;
   double ss = 0.0;
   for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
     f32x4 red[kUnroll];
     f32x4 old[kUnroll];
-    // Issue every load of this round before using any.
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int v = v0 + u * kBlock;
       if (v < nvec) {
-        if (C > 0) {
-          u32x2 raw[kC];
-#pragma unroll
-          for (int r = 0; r < kC; ++r) raw[r] = ld2u(c.g + int64_t(r) * c.stride + 4 * v);
-          red[u] = widen4(raw[0]);
-#pragma unroll
-          for (int r = 1; r < kC; ++r) red[u] = red[u] + widen4(raw[r]);
-        } else {
-          red[u] = widen4(ld2u(c.g + 4 * v));
-          for (int r = 1; r < c.slots; ++r) red[u] = red[u] + widen4(ld2u(c.g + int64_t(r) * c.stride + 4 * v));
-        }
+        red[u] = In::widen(In::load(c.g, c.off + 4 * v));
+        for (int r = 1; r < c.slots; ++r)
+          red[u] = red[u] + In::widen(In::load(c.g, int64_t(r) * c.stride + c.off + 4 * v));
         if (!c.first) old[u] = ld4f(c.acc + 4 * v);
       }
     }
@@ -227,7 +251,7 @@ __device__ double accumulate_generic(const AccChunk& c) {
       }
     }
   }
-  return ss + accumulate_tail(c, nvec);
+  return ss + accumulate_tail<In>(c, nvec);
 }
 
 // A full chunk (len == kChunkElems) with every choice fixed at compile time:
@@ -235,7 +259,7 @@ __device__ double accumulate_generic(const AccChunk& c) {
 // R = 2), FIRST whether the window starts here, WM the window division for
 // the fused norm (kNoDiv = no norm).  Same operations, same order as
 // accumulate_generic, without bounds checks or per-element branches.
-template <int C, int RM, bool FIRST, int WM>
+template <typename In, int C, int RM, bool FIRST, int WM>
 __device__ double accumulate_full(const AccChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   static_assert(nvec % (kUnroll * kBlock) == 0, "full chunks are whole rounds");
@@ -247,13 +271,13 @@ __device__ double accumulate_full(const AccChunk& c) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int v = v0 + u * kBlock;
-      u32x2 raw[C];
+      typename In::raw_t raw[C];
 #pragma unroll
-      for (int r = 0; r < C; ++r) raw[r] = ld2u(c.g + int64_t(r) * c.stride + 4 * v);
+      for (int r = 0; r < C; ++r) raw[r] = In::load(c.g, int64_t(r) * c.stride + c.off + 4 * v);
       if (!FIRST) old[u] = ld4f(c.acc + 4 * v);
-      red[u] = widen4(raw[0]);
+      red[u] = In::widen(raw[0]);
 #pragma unroll
-      for (int r = 1; r < C; ++r) red[u] = red[u] + widen4(raw[r]);
+      for (int r = 1; r < C; ++r) red[u] = red[u] + In::widen(raw[r]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -276,17 +300,25 @@ __device__ double accumulate_full(const AccChunk& c) {
   return ss;
 }
 
-template <int C, int RM>
+template <typename In, int C, int RM>
 __device__ double accumulate_full_dispatch(const AccChunk& c) {
   const int wm = c.fuse ? div_mode(c.wdiv) : kNoDiv;
   if (c.first) {
-    if (wm == kNoDiv) return accumulate_full<C, RM, true, kNoDiv>(c);
-    if (wm == kMulInv) return accumulate_full<C, RM, true, kMulInv>(c);
-    return accumulate_full<C, RM, true, kIeeeDiv>(c);
+    if (wm == kNoDiv) return accumulate_full<In, C, RM, true, kNoDiv>(c);
+    if (wm == kMulInv) return accumulate_full<In, C, RM, true, kMulInv>(c);
+    return accumulate_full<In, C, RM, true, kIeeeDiv>(c);
   }
-  if (wm == kNoDiv) return accumulate_full<C, RM, false, kNoDiv>(c);
-  if (wm == kMulInv) return accumulate_full<C, RM, false, kMulInv>(c);
-  return accumulate_full<C, RM, false, kIeeeDiv>(c);
+  if (wm == kNoDiv) return accumulate_full<In, C, RM, false, kNoDiv>(c);
+  if (wm == kMulInv) return accumulate_full<In, C, RM, false, kMulInv>(c);
+  return accumulate_full<In, C, RM, false, kIeeeDiv>(c);
+}
+
+template <typename In>
+__device__ double accumulate_chunk(const AccChunk& c) {
+  if (c.len == kChunkElems && c.slots == 1 && !c.mean) return accumulate_full_dispatch<In, 1, kNoDiv>(c);
+  if (c.len == kChunkElems && c.slots == 2 && !c.mean) return accumulate_full_dispatch<In, 2, kNoDiv>(c);
+  if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2) return accumulate_full_dispatch<In, 2, kMulInv>(c);
+  return accumulate_generic<In>(c);
 }
 
 __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P) {
@@ -295,7 +327,8 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
   const ChunkDev ch = P.chunks[q];
   const BucketDev bk = P.buckets[ch.bucket];
   AccChunk c;
-  c.g = P.grads[ch.bucket - P.b_first] + (ch.begin - bk.base);
+  c.g = P.grads[ch.bucket - P.b_first];
+  c.off = ch.begin - bk.base;
   c.stride = bk.stride;
   c.acc = P.acc + ch.begin;
   c.len = ch.len;
@@ -305,19 +338,7 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
   c.fuse = P.fuse_norm != 0;
   c.rdiv = make_divisor(P.R);
   c.wdiv = make_divisor(P.window > 0 ? P.window : 1);
-  double ss;
-  if (c.len == kChunkElems && c.slots == 1 && !c.mean)
-    ss = accumulate_full_dispatch<1, kNoDiv>(c);
-  else if (c.len == kChunkElems && c.slots == 2 && !c.mean)
-    ss = accumulate_full_dispatch<2, kNoDiv>(c);
-  else if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2)
-    ss = accumulate_full_dispatch<2, kMulInv>(c);
-  else if (c.slots == 1)
-    ss = accumulate_generic<1>(c);
-  else if (c.slots == 2)
-    ss = accumulate_generic<2>(c);
-  else
-    ss = accumulate_generic<0>(c);
+  const double ss = bk.grad_fp32 ? accumulate_chunk<F32In>(c) : accumulate_chunk<Bf16In>(c);
   if (c.fuse) {
     const double t = block_sum(ss);
     if (threadIdx.x == 0) P.partials[q] = t;
@@ -340,17 +361,19 @@ struct WinChunk {
   bool mean;
   Divisor rdiv;
   Divisor wdiv;
-  __device__ const uint16_t* g(int k) const { return P->grads[k * P->n_buckets + j] + off; }
+  __device__ const void* g(int k) const { return P->grads[k * P->n_buckets + j]; }
 };
 
+template <typename In>
 __device__ __forceinline__ float win_reduce1(const WinChunk& c, int k, int i) {
-  const uint16_t* g = c.g(k);
-  float s = widen1(g[i]);
-  for (int r = 1; r < c.slots; ++r) s = s + widen1(g[int64_t(r) * c.stride + i]);
+  const void* g = c.g(k);
+  float s = In::load1(g, c.off + i);
+  for (int r = 1; r < c.slots; ++r) s = s + In::load1(g, int64_t(r) * c.stride + c.off + i);
   return c.mean ? divide(s, c.rdiv) : s;
 }
 
 // Any chunk, any slot count: runtime checks, same order.
+template <typename In>
 __device__ double window_generic(const WinChunk& c) {
   const int n = c.P->n_micro;
   const int nvec = c.len >> 2;
@@ -358,9 +381,9 @@ __device__ double window_generic(const WinChunk& c) {
   for (int v = threadIdx.x; v < nvec; v += kBlock) {
     f32x4 acc;
     for (int k = 0; k < n; ++k) {
-      const uint16_t* g = c.g(k);
-      f32x4 red = widen4(ld2u(g + 4 * v));
-      for (int r = 1; r < c.slots; ++r) red = red + widen4(ld2u(g + int64_t(r) * c.stride + 4 * v));
+      const void* g = c.g(k);
+      f32x4 red = In::widen(In::load(g, c.off + 4 * v));
+      for (int r = 1; r < c.slots; ++r) red = red + In::widen(In::load(g, int64_t(r) * c.stride + c.off + 4 * v));
       if (c.mean) {
         red.x = divide(red.x, c.rdiv);
         red.y = divide(red.y, c.rdiv);
@@ -377,8 +400,8 @@ __device__ double window_generic(const WinChunk& c) {
   }
   if ((c.len & 3) && int(threadIdx.x) == nvec % kBlock) {
     for (int i = nvec * 4; i < c.len; ++i) {
-      float a = win_reduce1(c, 0, i);
-      for (int k = 1; k < n; ++k) a = a + win_reduce1(c, k, i);
+      float a = win_reduce1<In>(c, 0, i);
+      for (int k = 1; k < n; ++k) a = a + win_reduce1<In>(c, k, i);
       c.acc[i] = a;
       ss += sq(divide(a, c.wdiv));
     }
@@ -387,9 +410,9 @@ __device__ double window_generic(const WinChunk& c) {
 }
 
 // A full chunk with C slots, the MEAN divisor mode RM and the window
-// divisor mode WM fixed at compile time.  Microbatch k+1's loads are issued
-// before microbatch k's data is consumed.
-template <int C, int RM, int WM>
+// divisor mode WM fixed at compile time, any window length.  Microbatch
+// k+1's loads are issued before microbatch k's data is consumed.
+template <typename In, int C, int RM, int WM>
 __device__ double window_full(const WinChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   const int n = c.P->n_micro;
@@ -397,28 +420,28 @@ __device__ double window_full(const WinChunk& c) {
 #pragma unroll 1
   for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
     f32x4 acc[kUnroll];
-    u32x2 cur[kUnroll][C], nxt[kUnroll][C];
+    typename In::raw_t cur[kUnroll][C], nxt[kUnroll][C];
     {
-      const uint16_t* g = c.g(0);
+      const void* g = c.g(0);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int r = 0; r < C; ++r) cur[u][r] = ld2u(g + int64_t(r) * c.stride + 4 * (v0 + u * kBlock));
+        for (int r = 0; r < C; ++r) cur[u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
     }
 #pragma unroll 1
     for (int k = 0; k < n; ++k) {
       if (k + 1 < n) {
-        const uint16_t* g = c.g(k + 1);
+        const void* g = c.g(k + 1);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-          for (int r = 0; r < C; ++r) nxt[u][r] = ld2u(g + int64_t(r) * c.stride + 4 * (v0 + u * kBlock));
+          for (int r = 0; r < C; ++r) nxt[u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        f32x4 red = widen4(cur[u][0]);
+        f32x4 red = In::widen(cur[u][0]);
 #pragma unroll
-        for (int r = 1; r < C; ++r) red = red + widen4(cur[u][r]);
+        for (int r = 1; r < C; ++r) red = red + In::widen(cur[u][r]);
         red.x = divide_m<RM>(red.x, c.rdiv);
         red.y = divide_m<RM>(red.y, c.rdiv);
         red.z = divide_m<RM>(red.z, c.rdiv);
@@ -444,29 +467,29 @@ __device__ double window_full(const WinChunk& c) {
 
 // Common window lengths: every microbatch's loads are issued before any
 // is consumed (N * C * kUnroll loads in flight per lane).
-template <int C, int RM, int WM, int N>
+template <typename In, int C, int RM, int WM, int N>
 __device__ double window_full_n(const WinChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   double ss = 0.0;
 #pragma unroll 1
   for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    u32x2 raw[N][kUnroll][C];
+    typename In::raw_t raw[N][kUnroll][C];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-      const uint16_t* g = c.g(k);
+      const void* g = c.g(k);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int r = 0; r < C; ++r) raw[k][u][r] = ld2u(g + int64_t(r) * c.stride + 4 * (v0 + u * kBlock));
+        for (int r = 0; r < C; ++r) raw[k][u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       f32x4 acc;
 #pragma unroll
       for (int k = 0; k < N; ++k) {
-        f32x4 red = widen4(raw[k][u][0]);
+        f32x4 red = In::widen(raw[k][u][0]);
 #pragma unroll
-        for (int r = 1; r < C; ++r) red = red + widen4(raw[k][u][r]);
+        for (int r = 1; r < C; ++r) red = red + In::widen(raw[k][u][r]);
         red.x = divide_m<RM>(red.x, c.rdiv);
         red.y = divide_m<RM>(red.y, c.rdiv);
         red.z = divide_m<RM>(red.z, c.rdiv);
@@ -483,20 +506,30 @@ __device__ double window_full_n(const WinChunk& c) {
   return ss;
 }
 
-template <int C, int RM, int WM>
+template <typename In, int C, int RM, int WM>
 __device__ double window_full_w(const WinChunk& c) {
+  // FP32 contributions take twice the registers: keep them double-buffered.
+  if (sizeof(typename In::raw_t) > 8) return window_full<In, C, RM, WM>(c);
   switch (c.P->n_micro) {
-    case 2: return window_full_n<C, RM, WM, 2>(c);
-    case 3: return window_full_n<C, RM, WM, 3>(c);
-    case 4: return window_full_n<C, RM, WM, 4>(c);
-    case 8: return window_full_n<C, RM, WM, 8>(c);
-    default: return window_full<C, RM, WM>(c);
+    case 2: return window_full_n<In, C, RM, WM, 2>(c);
+    case 3: return window_full_n<In, C, RM, WM, 3>(c);
+    case 4: return window_full_n<In, C, RM, WM, 4>(c);
+    case 8: return window_full_n<In, C, RM, WM, 8>(c);
+    default: return window_full<In, C, RM, WM>(c);
   }
 }
 
-template <int C, int RM>
+template <typename In, int C, int RM>
 __device__ double window_full_dispatch(const WinChunk& c) {
-  return c.wdiv.pow2 ? window_full_w<C, RM, kMulInv>(c) : window_full_w<C, RM, kIeeeDiv>(c);
+  return c.wdiv.pow2 ? window_full_w<In, C, RM, kMulInv>(c) : window_full_w<In, C, RM, kIeeeDiv>(c);
+}
+
+template <typename In>
+__device__ double window_chunk(const WinChunk& c) {
+  if (c.len == kChunkElems && c.slots == 1 && !c.mean) return window_full_dispatch<In, 1, kNoDiv>(c);
+  if (c.len == kChunkElems && c.slots == 2 && !c.mean) return window_full_dispatch<In, 2, kNoDiv>(c);
+  if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2) return window_full_dispatch<In, 2, kMulInv>(c);
+  return window_generic<In>(c);
 }
 
 __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch P) {
@@ -515,15 +548,7 @@ __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch
   c.mean = bk.owner == GRO_OWNER_MEAN;
   c.rdiv = make_divisor(P.R);
   c.wdiv = make_divisor(P.n_micro);
-  double ss;
-  if (c.len == kChunkElems && c.slots == 1 && !c.mean)
-    ss = window_full_dispatch<1, kNoDiv>(c);
-  else if (c.len == kChunkElems && c.slots == 2 && !c.mean)
-    ss = window_full_dispatch<2, kNoDiv>(c);
-  else if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2)
-    ss = window_full_dispatch<2, kMulInv>(c);
-  else
-    ss = window_generic(c);
+  const double ss = bk.grad_fp32 ? window_chunk<F32In>(c) : window_chunk<Bf16In>(c);
   const double t = block_sum(ss);
   if (threadIdx.x == 0) P.partials[q] = t;
 }
@@ -717,10 +742,10 @@ template <int WM, bool BF16>
 __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
   constexpr int nvec = kChunkElems / 4;
 #pragma unroll 1
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    f32x4 a[kUnroll], p[kUnroll], m[kUnroll], w[kUnroll];
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnrollAdam * kBlock) {
+    f32x4 a[kUnrollAdam], p[kUnrollAdam], m[kUnrollAdam], w[kUnrollAdam];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollAdam; ++u) {
       const int v = v0 + u * kBlock;
       a[u] = ld4f(c.acc + 4 * v);
       p[u] = ld4f(c.p + 4 * v);
@@ -728,7 +753,7 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
       w[u] = ld4f(c.v + 4 * v);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollAdam; ++u) {
       const int v = v0 + u * kBlock;
       adamw4<WM>(a[u], p[u], m[u], w[u], k);
       st4f(c.p + 4 * v, p[u]);
@@ -742,7 +767,7 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
 // Chunks are visited last to first: the step's last accumulate pass has just
 // written the accumulator front to back, so its final stretch is still in
 // the MI355X's memory-side Infinity Cache when this pass starts.
-__global__ __launch_bounds__(kBlock) void k_adamw(const AdamWLaunch P) {
+__global__ __launch_bounds__(kBlock, GRO_ADAMW_MIN_BLOCKS) void k_adamw(const AdamWLaunch P) {
   const int64_t q = P.n_chunks - 1 - int64_t(blockIdx.x);
   if (q >= P.n_chunks) return;
   if (P.scalars[kFinite] == 0.0) return;  // non-finite norm: skip the step

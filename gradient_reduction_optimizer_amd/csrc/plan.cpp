@@ -11,8 +11,8 @@
 // Transformer Training", section "Backend split": rejection happens before
 // any work is done.
 //
-// Buckets hold one owner class and one decay setting each, so every chunk of
-// a bucket runs the same arithmetic; tensors are packed densely inside a
+// Buckets hold one owner class, one decay setting and one gradient type
+// each, so every chunk of a bucket runs the same arithmetic; tensors are packed densely inside a
 // bucket and only a tensor larger than the capacity is split.
 #include <cstdio>
 #include <cstring>
@@ -58,7 +58,7 @@ int classify(const gro_tensor_desc& d, int32_t R, gro_tensor_layout* lay) {
     numel *= s;
   }
   lay->numel = numel;
-  if (d.flags & ~(GRO_NO_DECAY | GRO_FROZEN))
+  if (d.flags & ~(GRO_NO_DECAY | GRO_FROZEN | GRO_FP32_GRAD))
     return set_error(GRO_E_PLACEMENT, "param_id %lld: unknown flags 0x%x",
                      (long long)d.param_id, d.flags);
   switch (d.placement) {
@@ -93,16 +93,19 @@ int classify(const gro_tensor_desc& d, int32_t R, gro_tensor_layout* lay) {
   lay->in_norm = 1;
   lay->updated = 1;
   lay->decayed = (d.flags & GRO_NO_DECAY) ? 0 : 1;
+  lay->grad_dtype = (d.flags & GRO_FP32_GRAD) ? GRO_GRAD_FP32 : GRO_GRAD_BF16;
   return GRO_OK;
 }
 
-void open_bucket(gro_plan* p, int64_t base, int32_t owner, int32_t slots, int32_t decayed) {
+void open_bucket(gro_plan* p, int64_t base, int32_t owner, int32_t slots, int32_t decayed,
+                 int32_t grad_dtype) {
   gro_bucket_info b;
   std::memset(&b, 0, sizeof(b));
   b.flat_base = base;
   b.owner = owner;
   b.slots = slots;
   b.decayed = decayed;
+  b.grad_dtype = grad_dtype;
   p->buckets.push_back(b);
 }
 
@@ -152,12 +155,15 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
                              GRO_OWNER_LOCAL_REDUCED};
   for (int32_t owner : owners) {
     for (int32_t decayed = 1; decayed >= 0; --decayed) {
+     for (int32_t dtype = GRO_GRAD_BF16; dtype <= GRO_GRAD_FP32; ++dtype) {
       bool open = false;  // a bucket of this group accepts more tensors
       for (auto& t : p->tensors) {
-        if (t.owner != owner || t.decayed != decayed || t.numel == 0 || !t.updated) continue;
+        if (t.owner != owner || t.decayed != decayed || t.grad_dtype != dtype || t.numel == 0 ||
+            !t.updated)
+          continue;
         if (t.numel <= bucket_elems) {
           if (!open || p->buckets.back().len + t.numel > bucket_elems) {
-            open_bucket(p, align_up(pos, kAlignElems), owner, t.slots, decayed);
+            open_bucket(p, align_up(pos, kAlignElems), owner, t.slots, decayed, dtype);
             open = true;
           }
           gro_bucket_info& b = p->buckets.back();
@@ -174,7 +180,7 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
           t.n_buckets = 0;
           while (left > 0) {
             const int64_t piece = left < split ? left : split;
-            open_bucket(p, align_up(pos, kAlignElems), owner, t.slots, decayed);
+            open_bucket(p, align_up(pos, kAlignElems), owner, t.slots, decayed, dtype);
             p->buckets.back().len = piece;
             pos = p->buckets.back().flat_base + piece;
             left -= piece;
@@ -183,6 +189,7 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
           open = true;  // the last piece's bucket may take following tensors
         }
       }
+     }
     }
   }
   p->n_flat = align_up(pos, kAlignElems);
@@ -207,7 +214,7 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
     d.owner = bk.owner;
     d.slots = bk.slots;
     d.decayed = bk.decayed;
-    d.reserved = 0;
+    d.grad_fp32 = bk.grad_dtype == GRO_GRAD_FP32 ? 1 : 0;
     p->bucket_dev.push_back(d);
   }
 

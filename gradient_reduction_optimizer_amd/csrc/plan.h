@@ -34,7 +34,7 @@ struct BucketDev {         // 32 B
   int32_t owner;           // GRO_OWNER_*
   int32_t slots;
   int32_t decayed;
-  int32_t reserved;
+  int32_t grad_fp32;       // 1: FP32 gradient contributions, 0: BF16
 };
 static_assert(sizeof(ChunkDev) == 16, "chunk table entry is 16 bytes");
 static_assert(sizeof(BucketDev) == 32, "bucket table entry is 32 bytes");

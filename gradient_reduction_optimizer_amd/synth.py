@@ -39,6 +39,7 @@ class TensorSpec:
     shard_index: int = -1
     frozen: bool = False
     no_decay: bool = False
+    fp32_grad: bool = False       # contributions arrive in FP32 instead of BF16
 
     @property
     def numel(self) -> int:
@@ -225,6 +226,25 @@ def grad_bf16(w: Workload, tensor_index: int, micro: int, slot: int,
     n = w.tensors[tensor_index].numel if numel is None else numel
     seed = stream_seed(w.seed, _GRAD, tensor_index, micro, slot)
     return _normal(n, w.sigma, seed, device).to(torch.bfloat16)
+
+
+def grad_contribution(w: Workload, tensor_index: int, micro: int, slot: int, device="cpu"):
+    """Gradient contribution in the tensor's own type: BF16 as grad_bf16,
+    or the FP32 normals themselves for an fp32_grad tensor."""
+    import torch
+    t = w.tensors[tensor_index]
+    if not t.fp32_grad:
+        return grad_bf16(w, tensor_index, micro, slot, device=device)
+    seed = stream_seed(w.seed, _GRAD, tensor_index, micro, slot)
+    return _normal(t.numel, w.sigma, seed, device)
+
+
+def host_values(t) -> np.ndarray:
+    """Host copy for the oracle: uint16 bits for BF16, float32 otherwise."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.detach().cpu().numpy().astype(np.float32, copy=True)
 
 
 def master_init(w: Workload, tensor_index: int, device="cpu"):

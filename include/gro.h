@@ -71,8 +71,13 @@ extern "C" {
 #define GRO_REDUCED   3  /* already reduced by another owner: used as is */
 
 /* ---- per-tensor flags ---- */
-#define GRO_NO_DECAY 1u  /* no weight decay for this tensor */
-#define GRO_FROZEN   2u  /* no gradient, not in the norm, not updated */
+#define GRO_NO_DECAY  1u  /* no weight decay for this tensor */
+#define GRO_FROZEN    2u  /* no gradient, not in the norm, not updated */
+#define GRO_FP32_GRAD 4u  /* gradient contributions arrive in FP32 instead of BF16 */
+
+/* ---- gradient element types (gro_tensor_layout / gro_bucket_info) ---- */
+#define GRO_GRAD_BF16 0
+#define GRO_GRAD_FP32 1
 
 /* ---- owner classes reported by gro_plan_tensor / gro_plan_bucket ---- */
 #define GRO_OWNER_MEAN          0
@@ -126,11 +131,12 @@ typedef struct gro_tensor_layout {
   int32_t decayed;
   int32_t first_bucket;     /* -1 when the tensor has no elements in a bucket */
   int32_t n_buckets;
-  int32_t reserved;
+  int32_t grad_dtype;       /* GRO_GRAD_BF16 or GRO_GRAD_FP32 */
 } gro_tensor_layout;
 
-/* A bucket: flat range [flat_base, flat_base+len) of one owner class and one
- * decay setting.  Its gradient buffer is BF16 [slots][slot_stride]: element
+/* A bucket: flat range [flat_base, flat_base+len) of one owner class, one
+ * decay setting and one gradient type.  Its gradient buffer is
+ * [slots][slot_stride] elements of that type (BF16 or FP32): element
  * flat_base+i of slot r is at index r*slot_stride + i. */
 typedef struct gro_bucket_info {
   int64_t flat_base;
@@ -141,7 +147,7 @@ typedef struct gro_bucket_info {
   int32_t owner;
   int32_t slots;
   int32_t decayed;
-  int32_t reserved;
+  int32_t grad_dtype;       /* GRO_GRAD_BF16 or GRO_GRAD_FP32 */
 } gro_bucket_info;
 
 /* AdamW hyper-parameters as the user states them (FP64).  Per-step scalars
@@ -158,8 +164,8 @@ typedef struct gro_adamw_hparams {
  * param_id; duplicates -> GRO_E_DUPLICATE; bad placement/shard_index/flags ->
  * GRO_E_PLACEMENT; R < 1, n_tensors < 0, ndim out of [0,8], negative dims,
  * bucket_elems < 64 -> GRO_E_INVALID), then the layout: tensors grouped by
- * (owner class, decay) in the order MEAN, SUM, LOCAL_SHARD, LOCAL_REDUCED,
- * descriptor order within a group, packed into buckets of at most
+ * (owner class, decay, gradient type) in the order MEAN, SUM, LOCAL_SHARD,
+ * LOCAL_REDUCED (decayed first, BF16 first), descriptor order within a group, packed into buckets of at most
  * bucket_elems elements; only a tensor larger than the capacity is split.
  * Host only, deterministic.  On success *out owns the host tables. */
 int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors, int32_t R,

@@ -133,13 +133,24 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     return out.astype(np.uint16)
 
 
+def as_f32(x: np.ndarray) -> np.ndarray:
+    """A gradient contribution as FP32: BF16 bits widened, FP32 as is."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_to_f32(x)
+    if x.dtype == np.float32:
+        return x
+    raise TypeError(f"gradient contributions are BF16 bits (uint16) or float32, not {x.dtype}")
+
+
 # ---------------------------------------------------- O2 reduce, accumulate
 def reduce_contributions(owner: Owner, R: int, slots: Sequence[np.ndarray]) -> np.ndarray:
     """One microbatch's reduced FP32 gradient for one parameter.
 
-    The ``owner.slots`` BF16 contributions are widened and summed in FP32 in
-    rank order 0..c-1 (P1 "Preserved prototype and evidence": FP32
-    reduction).  MEAN then divides by R (the average over TP ranks, P1 "Why
+    The ``owner.slots`` contributions -- BF16 bit patterns (uint16 arrays),
+    widened exactly, or FP32 arrays, used as they are (P1 "Proposed scope
+    and acceptance criteria": BF16/FP32) -- are summed in FP32 in rank order
+    0..c-1 (P1 "Preserved prototype and evidence": FP32 reduction).  MEAN then divides by R (the average over TP ranks, P1 "Why
     this needs separate work"); SUM keeps the sum; a LOCAL owner's single
     contribution is used as it is.
     """
@@ -147,9 +158,9 @@ def reduce_contributions(owner: Owner, R: int, slots: Sequence[np.ndarray]) -> n
         raise ValueError("an excluded parameter has no gradient")
     if len(slots) != owner.slots:
         raise ValueError(f"expected {owner.slots} contributions, got {len(slots)}")
-    s = bf16_to_f32(slots[0])
+    s = as_f32(slots[0])
     for r in range(1, owner.slots):
-        s = s + bf16_to_f32(slots[r])
+        s = s + as_f32(slots[r])
     if owner.owner == MEAN:
         s = s / F32(R)
     return s
@@ -310,7 +321,7 @@ def optimizer_window(owners: Sequence[Owner], R: int, micro_grads, master, m, v,
 
 __all__ = [
     "MEAN", "SUM", "LOCAL_SHARD", "LOCAL_REDUCED", "EXCLUDED", "OWNERS",
-    "Rejected", "Owner", "assign_owners", "bf16_to_f32", "f32_to_bf16",
+    "Rejected", "Owner", "assign_owners", "bf16_to_f32", "f32_to_bf16", "as_f32",
     "reduce_contributions", "accumulate", "window_gradient", "global_norm",
     "clip_coefficient", "AdamWScalars", "adamw_scalars", "adamw_update",
     "WindowResult", "optimizer_window",

@@ -106,9 +106,10 @@ class Case:
                 out.append(None)
                 continue
             if self.w.tensors[i].numel == 0:
-                out.append([torch.zeros(0, dtype=torch.bfloat16, device=self.device)] * o.slots)
+                dt = torch.float32 if self.w.tensors[i].fp32_grad else torch.bfloat16
+                out.append([torch.zeros(0, dtype=dt, device=self.device)] * o.slots)
                 continue
-            out.append([synth.grad_bf16(self.w, i, 1000 * step + k, r, device=self.device)
+            out.append([synth.grad_contribution(self.w, i, 1000 * step + k, r, device=self.device)
                         for r in range(o.slots)])
         return out
 
@@ -194,7 +195,7 @@ def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[flo
                 micro.append(g)
             else:
                 c.gpu_accumulate(g, k, n, fuse=fuse, bucket_order=bucket_order)
-            grads_host.append([None if x is None else [bits16(s) for s in x] for x in g])
+            grads_host.append([None if x is None else [synth.host_values(s) for s in x] for x in g])
         if window_call:
             c.gpu_accumulate_window(micro, n)
         norm, norm_sq, finite = c.gpu_finish(n, step, max_norm)

@@ -412,6 +412,34 @@ def pin_bf16(M):
         assert np.array_equal(got[~xn], want[~xn])
 
 
+# ---------------------------------------------- FP32 contributions
+def pin_fp32_contributions(M):
+    """FP32 contributions (P1 acceptance matrix: BF16/FP32): partial sums of
+    the head- and sequence-sharded layers match the unsharded gradient within
+    FP32 rounding; two identical FP32 replicas average to the replica exactly;
+    a local FP32 gradient passes through bit for bit."""
+    for full, parts in (_head_sharded_qk_norm_case(), _sequence_sharded_linear_case()):
+        f32 = [p.astype(np.float32) for p in parts]
+        o = M.assign_owners([spec(0, full.shape, "partial")], 2)[0]
+        red = M.reduce_contributions(o, 2, f32).astype(np.float64)
+        bound = sum(np.abs(p) for p in parts) * 2.0 ** -22 + 1e-12
+        assert np.all(np.abs(red - full) <= bound), np.max(np.abs(red - full) / bound)
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(5000) * 1e-2).astype(np.float32)
+    x[:4] = [0.0, -0.0, 1e-40, -1.5e38]  # |x| below half the FP32 maximum: x + x is exact
+    o = M.assign_owners([spec(0, x.shape, "replicate")], 2)[0]
+    red = M.reduce_contributions(o, 2, [x, x.copy()])
+    assert np.array_equal(red.view(np.uint32), x.view(np.uint32))
+    for placement in ("shard", "reduced"):
+        o = M.assign_owners([spec(0, x.shape, placement)], 2)[0]
+        red = M.reduce_contributions(o, 2, [x])
+        assert np.array_equal(red.view(np.uint32), x.view(np.uint32))
+    # FP32 values are not rounded to BF16 on the way in
+    y = np.array([1.0 + 2.0 ** -20], dtype=np.float32)
+    o = M.assign_owners([spec(0, y.shape, "shard")], 2)[0]
+    assert M.reduce_contributions(o, 2, [y])[0] == y[0]
+
+
 PINS = [
     pin_ownership_table,
     pin_ownership_rejections,
@@ -426,4 +454,5 @@ PINS = [
     pin_adamw_matches_torch,
     pin_clip_then_adamw_matches_torch,
     pin_bf16,
+    pin_fp32_contributions,
 ]

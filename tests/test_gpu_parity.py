@@ -37,7 +37,7 @@ def _spec(pid, shape, placement, shard_index=None, frozen=False, no_decay=False)
                             frozen=frozen, no_decay=no_decay)
 
 
-def ragged_workload(R=2, seed=7, bucket_elems=25_000_000, sizes=None):
+def ragged_workload(R=2, seed=7, bucket_elems=25_000_000, sizes=None, fp32_every=0):
     """Odd-sized tensors of every placement spanning several chunks, plus a
     frozen and a no-decay tensor."""
     rng = np.random.default_rng(seed)
@@ -49,6 +49,7 @@ def ragged_workload(R=2, seed=7, bucket_elems=25_000_000, sizes=None):
         pl = synth.PLACEMENTS[i % 4]
         tensors.append(_spec(i, (n,), pl, shard_index=(i % R) if pl == "shard" else -1,
                              no_decay=(i % 5 == 3)))
+        tensors[-1].fp32_grad = bool(fp32_every) and i % fp32_every == 1
     tensors.append(_spec(len(sizes), (33, 17), "replicate", frozen=True))
     tensors.append(_spec(len(sizes) + 1, (0, 4), "partial"))
     return synth.Workload("ragged", tensors, R=R, windows=[3], sigma=1e-2, seed=seed,
@@ -138,6 +139,21 @@ def test_window_call_tiny_and_many_buckets():
         assert_parity(cmps, norms)
         for k in cmps.values():
             assert k.n_diff_bits == 0, str(k)
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+@pytest.mark.parametrize("window_call", [False, True])
+def test_fp32_gradient_contributions(R, window_call):
+    """Tensors whose contributions arrive in FP32 (their own buckets) next to
+    BF16 ones, per-microbatch and window calls."""
+    w = ragged_workload(R=R, fp32_every=2, bucket_elems=30000)
+    assert any(t.fp32_grad for t in w.tensors) and not all(t.fp32_grad for t in w.tensors)
+    log(f"case fp32 contributions R={R} window_call={window_call}")
+    c, cmps, norms = run_parity(w, [3, 2, 8], window_call=window_call, log=log)
+    assert any(bk["grad_dtype"] == B.GRO_GRAD_FP32 for bk in c.plan.buckets)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
 
 
 @pytest.mark.parametrize("max_norm", [0.0, float("inf"), -1.0, 1e-3, 1e9])

@@ -11,7 +11,7 @@ F32 = np.float32
 _orig = {name: getattr(M, name) for name in (
     "assign_owners", "reduce_contributions", "accumulate", "window_gradient",
     "global_norm", "clip_coefficient", "adamw_scalars", "adamw_update", "f32_to_bf16",
-    "bf16_to_f32")}
+    "bf16_to_f32", "as_f32")}
 
 
 def _partial_as_replicate(tensors, R):
@@ -145,6 +145,13 @@ def _ties_away(x):
     return out.astype(np.uint16)
 
 
+def _fp32_through_bf16(x):
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        return M.bf16_to_f32(M.f32_to_bf16(x))
+    return _orig["as_f32"](x)
+
+
 def _widen_wrong_shift(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)).view(F32)
 
@@ -174,6 +181,7 @@ MUTANTS = {
     "bf16_truncates": ("f32_to_bf16", _truncate_bf16),
     "bf16_ties_away": ("f32_to_bf16", _ties_away),
     "widen_wrong_shift": ("bf16_to_f32", _widen_wrong_shift),
+    "fp32_rounded_to_bf16": ("as_f32", _fp32_through_bf16),
 }
 
 

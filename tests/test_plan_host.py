@@ -80,6 +80,7 @@ def _check_layout(plan, tensors, cap):
         for b, _, _, _ in segs:
             bk = buckets[b]
             assert bk["owner"] == t["owner"] and bk["decayed"] == t["decayed"] and bk["slots"] == t["slots"]
+            assert bk["grad_dtype"] == t["grad_dtype"]
         # only tensors larger than the capacity are split
         assert (t["n_buckets"] > 1) == (t["numel"] > cap)
     spans.sort()
@@ -100,7 +101,7 @@ def _check_layout(plan, tensors, cap):
             bmerged.append([a, b])
     assert merged == bmerged, "tensors do not exactly cover the buckets"
     # owner classes appear in the fixed order MEAN, SUM, LOCAL_SHARD, LOCAL_REDUCED
-    keys = [(bk["owner"], -bk["decayed"]) for bk in buckets]
+    keys = [(bk["owner"], -bk["decayed"], bk["grad_dtype"]) for bk in buckets]
     assert keys == sorted(keys)
 
 
@@ -133,11 +134,11 @@ def test_small_bucket_caps_split_large_tensors(cap):
     assert plan.info["n_buckets"] > 4
 
 
-def _spec(pid, shape, placement, shard_index=None, frozen=False, no_decay=False):
+def _spec(pid, shape, placement, shard_index=None, frozen=False, no_decay=False, fp32_grad=False):
     if shard_index is None:
         shard_index = 0 if placement == "shard" else -1
     return SimpleNamespace(param_id=pid, shape=tuple(shape), placement=placement,
-                           shard_index=shard_index, frozen=frozen, no_decay=no_decay)
+                           shard_index=shard_index, frozen=frozen, no_decay=no_decay, fp32_grad=fp32_grad)
 
 
 def test_random_descriptor_sets_match_oracle():
@@ -152,7 +153,8 @@ def test_random_descriptor_sets_match_oracle():
             pl = synth.PLACEMENTS[int(rng.integers(0, 4))]
             tensors.append(_spec(int(rng.integers(0, 1 << 40)) * 64 + i, shape, pl,
                                  shard_index=int(rng.integers(0, R)) if pl == "shard" else -1,
-                                 frozen=bool(rng.random() < 0.1), no_decay=bool(rng.random() < 0.3)))
+                                 frozen=bool(rng.random() < 0.1), no_decay=bool(rng.random() < 0.3),
+                                 fp32_grad=bool(rng.random() < 0.3)))
         cap = int(rng.choice([64, 128, 200, 1000, 1 << 20]))
         _check_table(tensors, R, cap)
 
