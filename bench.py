@@ -63,7 +63,7 @@ def load_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(w, frac: float, log, windows: int = 2):
+def cpu_baseline(w, frac: float, log, windows: int = 4):
     """Time the CPU oracle (as it is) on a bounded sample of the workload:
     every non-Shard tensor plus Shard tensors in order up to `frac` of the
     elements; `windows` consecutive optimizer steps, each one full window
