@@ -35,7 +35,8 @@ GRO_MAX_NDIM = 8
 
 EXPORTS = ("gro_plan_create", "gro_plan_destroy", "gro_plan_get_info", "gro_plan_tensor",
            "gro_plan_bucket", "gro_plan_bind", "gro_accumulate", "gro_accumulate_window",
-           "gro_reduce_norm", "gro_plan_get_norm", "gro_clip_adamw", "gro_last_error")
+           "gro_reduce_norm", "gro_plan_get_norm", "gro_clip_adamw", "gro_init_uniform",
+           "gro_last_error")
 
 
 class gro_tensor_desc(ctypes.Structure):
@@ -102,6 +103,7 @@ def load() -> ctypes.CDLL:
     L.gro_reduce_norm.argtypes = [P, P, I32, P]
     L.gro_plan_get_norm.argtypes = [P, ctypes.POINTER(D), ctypes.POINTER(D), ctypes.POINTER(I32)]
     L.gro_clip_adamw.argtypes = [P, P, I32, D, ctypes.POINTER(gro_adamw_hparams), I64, P, P, P, P, P]
+    L.gro_init_uniform.argtypes = [P, ctypes.c_uint64, ctypes.POINTER(D), ctypes.POINTER(D), P, P, P]
     L.gro_last_error.argtypes = []
     L.gro_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -220,3 +222,14 @@ def gro_clip_adamw(plan: int, d_acc: int, window_size: int, max_norm: float, hp:
                                  float(max_norm), ctypes.byref(h), int(step), ctypes.c_void_p(d_master),
                                  ctypes.c_void_p(d_m), ctypes.c_void_p(d_v),
                                  ctypes.c_void_p(d_param_bf16 or 0), ctypes.c_void_p(stream)))
+
+
+def gro_init_uniform(plan: int, seed: int, bounds: Sequence[float], offsets: Optional[Sequence[float]],
+                     d_master: int, d_param_bf16: int = 0, stream: int = 0) -> None:
+    """bounds/offsets: one value per tensor, in descriptor order."""
+    n = max(len(bounds), 1)
+    b = (ctypes.c_double * n)(*[float(x) for x in bounds])
+    o = None if offsets is None else (ctypes.c_double * n)(*[float(x) for x in offsets])
+    _check(load().gro_init_uniform(ctypes.c_void_p(plan), ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), b, o,
+                                   ctypes.c_void_p(d_master), ctypes.c_void_p(d_param_bf16 or 0),
+                                   ctypes.c_void_p(stream)))

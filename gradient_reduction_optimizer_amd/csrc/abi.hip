@@ -12,8 +12,10 @@
 // updates.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "kernels.h"
 #include "plan.h"
@@ -237,6 +239,55 @@ extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_s
   p->norm_done = true;
   p->norm_window = window_size;
   p->norm_stream = stream;
+  return GRO_OK;
+}
+
+extern "C" int gro_init_uniform(gro_plan* p, uint64_t seed, const double* bounds, const double* offsets,
+                                float* d_master, uint16_t* d_param_bf16, void* stream) {
+  clear_error();
+  int rc = check_bound(p);
+  if (rc != GRO_OK) return rc;
+  const size_t nt = p->tensors.size();
+  if (nt > 0 && bounds == nullptr) return set_error(GRO_E_INVALID, "bounds is NULL");
+  if (!p->buckets.empty() && (d_master == nullptr || !aligned16(d_master) ||
+                              (d_param_bf16 != nullptr && !aligned16(d_param_bf16))))
+    return set_error(GRO_E_INVALID, "master / BF16 pointers must be 16-byte aligned (master non-NULL)");
+  std::vector<TensorDev>& tab = p->init_table;
+  tab.clear();
+  for (size_t i = 0; i < nt; ++i) {
+    const gro_tensor_layout& t = p->tensors[i];
+    const double b = bounds[i], o = offsets ? offsets[i] : 0.0;
+    if (!(b >= 0.0) || !std::isfinite(b) || !std::isfinite(o))
+      return set_error(GRO_E_INVALID, "tensor %zu: bound must be finite and >= 0, offset finite", i);
+    if (!t.updated || t.numel == 0) continue;
+    TensorDev d;
+    d.flat_offset = t.flat_offset;
+    d.numel = t.numel;
+    d.param_id = t.param_id;
+    d.index_base = t.owner == GRO_OWNER_LOCAL_SHARD ? int64_t(p->shard_index[i]) * t.numel : 0;
+    d.bound = float(b);
+    d.offset = float(o);
+    d.reserved = 0;
+    tab.push_back(d);
+  }
+  std::sort(tab.begin(), tab.end(),
+            [](const TensorDev& a, const TensorDev& b) { return a.flat_offset < b.flat_offset; });
+  if (tab.empty()) return GRO_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TensorDev* dtab = reinterpret_cast<TensorDev*>(p->d_ws + p->ws.tensor_off);
+  hipError_t e = hipMemcpyAsync(dtab, tab.data(), tab.size() * sizeof(TensorDev), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "init table upload");
+  InitLaunch a;
+  a.chunks = dev_chunks(p);
+  a.n_chunks = int64_t(p->chunks.size());
+  a.tensors = dtab;
+  a.n_tensors = int32_t(tab.size());
+  a.seed = seed;
+  a.master = d_master;
+  a.p_bf16 = d_param_bf16;
+  e = launch_init_uniform(a, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "init launch");
   return GRO_OK;
 }
 

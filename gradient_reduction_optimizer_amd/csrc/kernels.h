@@ -67,7 +67,18 @@ struct AdamWLaunch {
   float step_size, sqrt_bc2, eps, decay;
 };
 
+struct InitLaunch {
+  const ChunkDev* chunks;
+  int64_t n_chunks;
+  const TensorDev* tensors;   // sorted by flat offset
+  int32_t n_tensors;
+  uint64_t seed;
+  float* master;
+  uint16_t* p_bf16;           // may be null
+};
+
 hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s);
+hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s);
 hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s);
 hipError_t launch_norm_partials(const NormLaunch& a, hipStream_t s);
 hipError_t launch_norm_final(const double* partials, int64_t n_chunks, double* scalars,

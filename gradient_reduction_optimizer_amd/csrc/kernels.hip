@@ -810,9 +810,77 @@ __global__ __launch_bounds__(kBlock, GRO_ADAMW_MIN_BLOCKS) void k_adamw(const Ad
   }
 }
 
+// ---------------------------------------------- replica-consistent init
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 64x64->128-bit multiplies
+// with the key bumped by the Weyl constants between rounds.
+struct U64x4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ U64x4 philox4x64_10(U64x4 c, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c.w[0]), lo0 = M0 * c.w[0];
+    const uint64_t hi1 = __umul64hi(M1, c.w[2]), lo1 = M1 * c.w[2];
+    U64x4 n;
+    n.w[0] = hi1 ^ c.w[1] ^ k0;
+    n.w[1] = lo1;
+    n.w[2] = hi0 ^ c.w[3] ^ k1;
+    n.w[3] = lo0;
+    c = n;
+    k0 += W0;
+    k1 += W1;
+  }
+  return c;
+}
+
+// Element g of parameter pid: counter (g / 4, 0, 0, 0), key (seed, pid);
+// output word g % 4, top 24 bits -> u = k * 2^-24 in [0, 1) (exact), value
+// = offset + (2u - 1) * bound (2u - 1 is exact; one rounding each after).
+__device__ __forceinline__ float init_value(uint64_t seed, const TensorDev& t, int64_t i) {
+  const uint64_t g = uint64_t(t.index_base + i);
+  U64x4 c;
+  c.w[0] = g >> 2;
+  c.w[1] = c.w[2] = c.w[3] = 0;
+  const U64x4 o = philox4x64_10(c, seed, uint64_t(t.param_id));
+  const float u = float(o.w[g & 3] >> 40) * 0x1p-24f;
+  const float s = 2.0f * u - 1.0f;
+  return t.offset + s * t.bound;
+}
+
+// One workgroup per chunk; each element finds its tensor by binary search
+// over the flat offsets.  Elements of no updated tensor do not exist in a
+// chunk, so every search succeeds.
+__global__ __launch_bounds__(kBlock) void k_init_uniform(const InitLaunch P) {
+  const int64_t q = int64_t(blockIdx.x);
+  if (q >= P.n_chunks) return;
+  const ChunkDev ch = P.chunks[q];
+  for (int i = threadIdx.x; i < ch.len; i += kBlock) {
+    const int64_t f = ch.begin + i;
+    int lo = 0, hi = P.n_tensors - 1;
+    while (lo < hi) {  // last tensor whose flat_offset <= f
+      const int mid = (lo + hi + 1) >> 1;
+      if (P.tensors[mid].flat_offset <= f) lo = mid; else hi = mid - 1;
+    }
+    const TensorDev t = P.tensors[lo];
+    const float x = init_value(P.seed, t, f - t.flat_offset);
+    P.master[f] = x;
+    if (P.p_bf16) P.p_bf16[f] = bf16_bits(x);
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ launchers
+hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s) {
+  if (a.n_chunks <= 0 || a.n_tensors <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_init_uniform, dim3(unsigned(a.n_chunks)), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
   const int64_t blocks = (a.q_end - a.q_begin) + (a.q_begin & 7);

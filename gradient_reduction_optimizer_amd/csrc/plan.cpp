@@ -139,6 +139,7 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
       return set_error(GRO_E_DUPLICATE, "param_id %lld has a second owner",
                        (long long)tensors[i].param_id);
     }
+    p->shard_index.push_back(tensors[i].shard_index);
     const int rc = classify(tensors[i], R, &p->tensors[size_t(i)]);
     if (rc != GRO_OK) {
       delete p;
@@ -228,6 +229,8 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
   off = uint64_t(align_up(int64_t(off + p->chunks.size() * sizeof(ChunkDev)), 256));
   ws.partial_off = off;
   off = uint64_t(align_up(int64_t(off + p->chunks.size() * sizeof(double)), 256));
+  ws.tensor_off = off;
+  off = uint64_t(align_up(int64_t(off + p->tensors.size() * sizeof(TensorDev)), 256));
   ws.total = off;
 
   p->count.assign(p->buckets.size(), 0);

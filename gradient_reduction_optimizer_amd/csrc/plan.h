@@ -36,14 +36,26 @@ struct BucketDev {         // 32 B
   int32_t decayed;
   int32_t grad_fp32;       // 1: FP32 gradient contributions, 0: BF16
 };
+// Per-tensor entry for gro_init_uniform (sorted by flat offset, updated
+// tensors with at least one element).
+struct TensorDev {         // 48 B
+  int64_t flat_offset;
+  int64_t numel;
+  int64_t param_id;
+  int64_t index_base;      // this rank's first element in the unsharded tensor
+  float bound;
+  float offset;
+  int64_t reserved;
+};
 static_assert(sizeof(ChunkDev) == 16, "chunk table entry is 16 bytes");
+static_assert(sizeof(TensorDev) == 48, "tensor table entry is 48 bytes");
 static_assert(sizeof(BucketDev) == 32, "bucket table entry is 32 bytes");
 
 // Device scalars written by the norm's second stage.
 enum ScalarSlot { kNormSq = 0, kNorm = 1, kFinite = 2, kNumScalars = 8 };
 
 struct WorkspaceLayout {
-  uint64_t bucket_off = 0, chunk_off = 0, partial_off = 0, scalar_off = 0, total = 0;
+  uint64_t bucket_off = 0, chunk_off = 0, partial_off = 0, scalar_off = 0, tensor_off = 0, total = 0;
 };
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -62,6 +74,8 @@ struct gro_plan {
   std::vector<gro_bucket_info> buckets;
   std::vector<gro::BucketDev> bucket_dev;
   std::vector<gro::ChunkDev> chunks;
+  std::vector<int32_t> shard_index;    // per tensor, as given (-1 unless Shard)
+  std::vector<gro::TensorDev> init_table;  // host staging for gro_init_uniform
   gro::WorkspaceLayout ws;
 
   // Binding.

@@ -42,7 +42,8 @@
  *    a thread-local message (gro_last_error).  Validation precedes any device
  *    work.  Non-finite data is reported through gro_plan_get_norm's `finite`
  *    flag, not a return code, because device work is asynchronous.
- *  - Only gro_plan_bind and gro_plan_get_norm wait for the device.
+ *  - Only gro_plan_bind, gro_init_uniform and gro_plan_get_norm wait for the
+ *    device.
  *  - Not thread-safe per plan; distinct plans may be used from distinct
  *    threads.
  */
@@ -234,6 +235,23 @@ int gro_plan_get_norm(gro_plan* plan, double* norm, double* norm_sq, int32_t* fi
 int gro_clip_adamw(gro_plan* plan, const float* d_acc, int32_t window_size, double max_norm,
                    const gro_adamw_hparams* hp, int64_t step, float* d_master, float* d_m,
                    float* d_v, uint16_t* d_param_bf16, void* stream);
+
+/* Replica-consistent initialisation of the FP32 master shard (and the
+ * optional BF16 copy) of every updated parameter, independent of the rank,
+ * of the layout and of when it runs (NeMo Automodel issue #3857, section
+ * "Why this needs separate work": parameters may be initialised after
+ * parallelisation, and rank-specific training RNG must not become a common
+ * initialisation RNG -- this draws nothing from any other generator).
+ * Element i of parameter p gets offset_p + (2u - 1) * bound_p with u in
+ * [0, 1) in steps of 2^-24, from Philox4x64-10 with key (seed, param_id)
+ * and counter (g / 4, 0, 0, 0), word g % 4, top 24 bits, where g is the
+ * element's index in the unsharded parameter: shard_index * numel + i for a
+ * Shard tensor (equal dim-0 shards), i otherwise.  bounds[t] >= 0 and
+ * offsets[t] (host, n_tensors entries in descriptor order, FP64 rounded to
+ * FP32; NULL offsets = 0) -- e.g. offset 1, bound 0 for a norm weight.
+ * Waits for its own upload before returning. */
+int gro_init_uniform(gro_plan* plan, uint64_t seed, const double* bounds, const double* offsets,
+                     float* d_master, uint16_t* d_param_bf16, void* stream);
 
 /* Thread-local text of the last error ("" if none). */
 const char* gro_last_error(void);

@@ -268,6 +268,53 @@ def adamw_update(g: np.ndarray, coef, p: np.ndarray, m: np.ndarray, v: np.ndarra
     return p, m, v, f32_to_bf16(p)
 
 
+# ------------------------------------------------------------- N3 init
+_MASK64 = (1 << 64) - 1
+_PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
+_PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64-10 of Salmon, Moraes, Dror and Shaw ("Parallel random
+    numbers: as easy as 1, 2, 3", SC 2011), in Python integers: ten rounds;
+    each multiplies words 0 and 2 by the two round constants (128-bit
+    products), mixes the high halves with the other words and the key, and
+    bumps the key by the Weyl constants."""
+    c = [int(x) & _MASK64 for x in counter]
+    k = [int(x) & _MASK64 for x in key]
+    for _ in range(10):
+        p0 = _PHILOX_M[0] * c[0]
+        p1 = _PHILOX_M[1] * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k[0], p1 & _MASK64, (p0 >> 64) ^ c[3] ^ k[1], p0 & _MASK64]
+        k = [(k[0] + _PHILOX_W[0]) & _MASK64, (k[1] + _PHILOX_W[1]) & _MASK64]
+    return c
+
+
+def init_uniform(seed: int, param_id: int, index_base: int, indices, bound: float, offset: float) -> np.ndarray:
+    """Replica-consistent initial values of the given element indices of one
+    parameter (P1 "Why this needs separate work": initialisation after
+    parallelisation must not depend on rank-specific training RNG).
+
+    Element g (its index in the unsharded parameter, index_base + i) draws
+    word g % 4 of Philox4x64-10 with counter (g // 4, 0, 0, 0) and key
+    (seed, param_id); its top 24 bits give u = k * 2^-24 in [0, 1); the value
+    is offset + (2u - 1) * bound in FP32 (bound, offset rounded to FP32).
+    Pure Python: meant for small or sampled index sets.
+    """
+    b, o = F32(bound), F32(offset)
+    out = np.empty(len(indices), dtype=F32)
+    cache = {}
+    for j, i in enumerate(indices):
+        g = int(index_base) + int(i)
+        blk = cache.get(g >> 2)
+        if blk is None:
+            blk = cache[g >> 2] = philox4x64_10((g >> 2, 0, 0, 0), (seed, param_id))
+        u = F32(blk[g & 3] >> 40) * F32(2.0 ** -24)
+        s = F32(2.0) * u - F32(1.0)
+        out[j] = o + s * b
+    return out
+
+
 # ----------------------------------------------------------- whole window
 @dataclasses.dataclass
 class WindowResult:
@@ -324,5 +371,5 @@ __all__ = [
     "Rejected", "Owner", "assign_owners", "bf16_to_f32", "f32_to_bf16", "as_f32",
     "reduce_contributions", "accumulate", "window_gradient", "global_norm",
     "clip_coefficient", "AdamWScalars", "adamw_scalars", "adamw_update",
-    "WindowResult", "optimizer_window",
+    "WindowResult", "optimizer_window", "philox4x64_10", "init_uniform",
 ]

@@ -440,6 +440,39 @@ def pin_fp32_contributions(M):
     assert M.reduce_contributions(o, 2, [y])[0] == y[0]
 
 
+# ---------------------------------------------- N3 initialisation
+def pin_philox_matches_numpy(M):
+    """Philox4x64-10 equals numpy's Philox bit generator (which advances the
+    256-bit counter by one before each block)."""
+    rng = np.random.default_rng(22)
+    for _ in range(20):
+        c = [int(x) for x in rng.integers(1, 2 ** 63, size=4)]
+        k = [int(x) for x in rng.integers(0, 2 ** 63, size=2)]
+        bg = np.random.Philox(key=np.array(k, dtype=np.uint64),
+                              counter=np.array([c[0] - 1] + c[1:], dtype=np.uint64))
+        assert [int(x) for x in bg.random_raw(4)] == M.philox4x64_10(c, k)
+
+
+def pin_init_uniform(M):
+    """Values lie in [offset - bound, offset + bound), on the 2^-24 grid of
+    the unit interval; bound 0 gives exactly the offset; moments of 20,000
+    draws match U(-b, b); different param_ids give different streams."""
+    idx = np.arange(20000)
+    x = M.init_uniform(7, 11, 0, idx, 0.5, 0.0).astype(np.float64)
+    assert np.all(x >= -0.5) and np.all(x < 0.5)
+    u = (x / 0.5 + 1) / 2
+    assert np.all(u * 2 ** 24 == np.round(u * 2 ** 24))
+    assert abs(x.mean()) < 4 * 0.5 / np.sqrt(3 * 20000)
+    assert abs(x.var() - 0.25 / 3) < 0.01
+    ones = M.init_uniform(7, 3, 5, np.arange(100), 0.0, 1.0)
+    assert np.all(ones == 1.0)
+    y = M.init_uniform(7, 12, 0, idx[:1000], 0.5, 0.0)
+    assert np.count_nonzero(y == x[:1000].astype(np.float32)) < 5
+    # the index is the unsharded one: shard r of length n starts at r*n
+    full = M.init_uniform(9, 4, 0, np.arange(64), 0.1, 0.0)
+    assert np.array_equal(M.init_uniform(9, 4, 32, np.arange(32), 0.1, 0.0), full[32:])
+
+
 PINS = [
     pin_ownership_table,
     pin_ownership_rejections,
@@ -455,4 +488,6 @@ PINS = [
     pin_clip_then_adamw_matches_torch,
     pin_bf16,
     pin_fp32_contributions,
+    pin_philox_matches_numpy,
+    pin_init_uniform,
 ]

@@ -11,7 +11,7 @@ F32 = np.float32
 _orig = {name: getattr(M, name) for name in (
     "assign_owners", "reduce_contributions", "accumulate", "window_gradient",
     "global_norm", "clip_coefficient", "adamw_scalars", "adamw_update", "f32_to_bf16",
-    "bf16_to_f32", "as_f32")}
+    "bf16_to_f32", "as_f32", "philox4x64_10", "init_uniform")}
 
 
 def _partial_as_replicate(tensors, R):
@@ -152,6 +152,22 @@ def _fp32_through_bf16(x):
     return _orig["as_f32"](x)
 
 
+def _philox_nine_rounds(counter, key):
+    c = [int(x) for x in counter]
+    k = [int(x) for x in key]
+    MASK = (1 << 64) - 1
+    for _ in range(9):
+        p0 = 0xD2E7470EE14C6C93 * c[0]
+        p1 = 0xCA5A826395121157 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k[0], p1 & MASK, (p0 >> 64) ^ c[3] ^ k[1], p0 & MASK]
+        k = [(k[0] + 0x9E3779B97F4A7C15) & MASK, (k[1] + 0xBB67AE8584CAA73B) & MASK]
+    return c
+
+
+def _init_ignores_shard_offset(seed, param_id, index_base, indices, bound, offset):
+    return _orig["init_uniform"](seed, param_id, 0, indices, bound, offset)
+
+
 def _widen_wrong_shift(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)).view(F32)
 
@@ -182,6 +198,8 @@ MUTANTS = {
     "bf16_ties_away": ("f32_to_bf16", _ties_away),
     "widen_wrong_shift": ("bf16_to_f32", _widen_wrong_shift),
     "fp32_rounded_to_bf16": ("as_f32", _fp32_through_bf16),
+    "philox_nine_rounds": ("philox4x64_10", _philox_nine_rounds),
+    "init_ignores_shard_offset": ("init_uniform", _init_ignores_shard_offset),
 }
 
 
