@@ -178,7 +178,7 @@ class Case:
 
 def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[float] = None,
                fuse: bool = True, R: Optional[int] = None, bucket_order=None, window_call: bool = False,
-               log=print):
+               log=print, zero_tensors=()):
     """Run len(windows) optimizer steps on both sides and compare after each.
     window_call: use gro_accumulate_window (one call per window) instead of
     one gro_accumulate per microbatch."""
@@ -191,6 +191,8 @@ def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[flo
         micro = []
         for k in range(n):
             g = c.draw(step, k)
+            for i in zero_tensors:  # an unused parameter: zero contributions
+                g[i] = [torch.zeros_like(x) for x in g[i]]
             if window_call:
                 micro.append(g)
             else:

@@ -156,6 +156,22 @@ def test_fp32_gradient_contributions(R, window_call):
         assert k.n_diff_bits == 0, str(k)
 
 
+def test_unused_parameters_are_still_decayed_and_updated():
+    """An unused parameter contributes zero gradients (DDP semantics): it is
+    in the norm (adding 0), decayed and stepped like any other."""
+    w = ragged_workload()
+    zero = [i for i, t in enumerate(w.tensors) if not t.frozen and t.numel > 100][:3]
+    log(f"case unused parameters {zero}")
+    c, cmps, norms = run_parity(w, [2, 3], zero_tensors=zero, log=log)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+    m = host(c.st.m)
+    for i in zero:
+        off = c.plan.tensors[i]["flat_offset"]
+        assert not np.any(m[off:off + w.tensors[i].numel])   # m stays 0 for a zero gradient
+
+
 @pytest.mark.parametrize("max_norm", [0.0, float("inf"), -1.0, 1e-3, 1e9])
 def test_clip_settings(max_norm):
     w = synth.tiny()
