@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgro.so")
+CLIENT = os.path.join(BUILD, "abi_client")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -50,6 +51,13 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # A plain C client of the ABI (used by the tests): C compiler, HIP
+    # runtime headers and library, linked against libgro.so.
+    client = os.path.join(ROOT, "tests", "native", "abi_client.c")
+    if os.path.exists(client):
+        _run(["gcc", "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+              f"-I{ROCM}/include", client, "-o", CLIENT, f"-L{PKG}", "-lgro", f"-L{ROCM}/lib",
+              "-lamdhip64", "-Wl,-rpath,$ORIGIN/..", f"-Wl,-rpath,{ROCM}/lib"], verbose)
     return LIB
 
 
