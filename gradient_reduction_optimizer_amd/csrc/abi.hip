@@ -33,6 +33,11 @@ int hip_fail(hipError_t e, const char* what) {
 int check_bound(const gro_plan* p) {
   if (p == nullptr) return set_error(GRO_E_INVALID, "plan is NULL");
   if (!p->bound) return set_error(GRO_E_STATE, "plan is not bound to a workspace");
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device)
+    return set_error(GRO_E_STATE, "plan is bound on device %d, current device is %d", p->device, dev);
   return GRO_OK;
 }
 
@@ -80,6 +85,7 @@ extern "C" int gro_plan_bind(gro_plan* p, void* d_workspace, uint64_t bytes, voi
   p->d_ws = ws;
   p->bound = true;
   p->device = dev;
+  p->norm_valid = false;
   reset_window(p);
   return GRO_OK;
 }
@@ -237,6 +243,7 @@ extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_s
   if (err != hipSuccess) return hip_fail(err, "norm stage-2 launch");
   std::fill(p->partials_ready.begin(), p->partials_ready.end(), 1);
   p->norm_done = true;
+  p->norm_valid = true;
   p->norm_window = window_size;
   p->norm_stream = stream;
   return GRO_OK;
@@ -295,6 +302,7 @@ extern "C" int gro_plan_get_norm(gro_plan* p, double* norm, double* norm_sq, int
   clear_error();
   int rc = check_bound(p);
   if (rc != GRO_OK) return rc;
+  if (!p->norm_valid) return set_error(GRO_E_STATE, "no gro_reduce_norm since the plan was bound");
   hipStream_t s = static_cast<hipStream_t>(p->norm_stream);
   double host[kNumScalars];
   hipError_t e = hipStreamSynchronize(s);

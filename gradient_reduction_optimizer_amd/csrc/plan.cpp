@@ -194,6 +194,10 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
     }
   }
   p->n_flat = align_up(pos, kAlignElems);
+  if (p->n_flat / kChunkElems + int64_t(p->buckets.size()) + 8 > int64_t(INT32_MAX)) {
+    delete p;
+    return set_error(GRO_E_INVALID, "plan too large: more chunks than one launch grid addresses");
+  }
 
   // Chunks and device tables.
   for (size_t b = 0; b < p->buckets.size(); ++b) {

@@ -220,7 +220,10 @@ int gro_accumulate_window(gro_plan* plan, int32_t b0, int32_t b1, const void* co
 int gro_reduce_norm(gro_plan* plan, const float* d_acc, int32_t window_size, void* stream);
 
 /* Wait for the plan's stream and read the last norm.  Any out pointer may be
- * NULL.  finite = 0 when the norm is NaN or infinite. */
+ * NULL.  finite = 0 when the norm is NaN or infinite.  GRO_E_STATE before
+ * the first gro_reduce_norm after binding.
+ * Every device call (bind excepted) must run with the device the plan was
+ * bound on current, else GRO_E_STATE. */
 int gro_plan_get_norm(gro_plan* plan, double* norm, double* norm_sq, int32_t* finite);
 
 /* Clip + fused AdamW on every updated element, after gro_reduce_norm of the

@@ -271,6 +271,9 @@ def test_window_bookkeeping_errors():
     ptrs = [b.data_ptr() for b in c.bufs]
     h = c.plan.handle
     acc = c.st.acc.data_ptr()
+    with pytest.raises(B.GroError) as e:      # no norm computed yet
+        B.gro_plan_get_norm(h)
+    assert e.value.kind == "state"
     with pytest.raises(B.GroError) as e:      # skipping microbatch 0
         B.gro_accumulate(h, 0, nb, ptrs, acc, 1, 2, s)
     assert e.value.kind == "state"
