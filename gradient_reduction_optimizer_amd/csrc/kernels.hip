@@ -113,10 +113,27 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-__device__ __forceinline__ u32x2 ld2u(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void st4f(float* p, const f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-__device__ __forceinline__ void st2u(uint16_t* p, const u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+// Streaming variants with the non-temporal cache policy.  They are used for
+// every stream a step touches once -- the gradient contributions and
+// AdamW's p, m, v and BF16 copy -- so that these do not push the FP32
+// accumulator out of the memory-side Infinity Cache between the pass that
+// writes it and the AdamW pass that reads it, and so that AdamW leaves few
+// dirty lines for the next step's first pass to drain.  The accumulator
+// itself keeps the default policy.
+__device__ __forceinline__ u32x2 ld2u_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+__device__ __forceinline__ f32x4 ld4f_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ void st4f_nt(float* p, const f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st2u_nt(uint16_t* p, const u32x2 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
 
 // Sum over the workgroup in a fixed order: a wave64 butterfly (every lane
 // ends with the same bits because IEEE addition commutes), then the wave
@@ -146,10 +163,11 @@ __device__ __forceinline__ double sq(float x) {
 // ------------------------------------------------------ gradient inputs
 // A bucket's gradient contributions are BF16 (widened exactly) or FP32 (used
 // as they are); the element type is a template parameter of every path.
+// Vector loads of contributions are non-temporal (each is read once a step).
 struct Bf16In {
   typedef u32x2 raw_t;
   static __device__ __forceinline__ raw_t load(const void* base, int64_t e) {
-    return ld2u(static_cast<const uint16_t*>(base) + e);
+    return ld2u_nt(static_cast<const uint16_t*>(base) + e);
   }
   static __device__ __forceinline__ f32x4 widen(const raw_t r) { return widen4(r); }
   static __device__ __forceinline__ float load1(const void* base, int64_t i) {
@@ -159,7 +177,7 @@ struct Bf16In {
 struct F32In {
   typedef f32x4 raw_t;
   static __device__ __forceinline__ raw_t load(const void* base, int64_t e) {
-    return ld4f(static_cast<const float*>(base) + e);
+    return ld4f_nt(static_cast<const float*>(base) + e);
   }
   static __device__ __forceinline__ f32x4 widen(const raw_t r) { return r; }
   static __device__ __forceinline__ float load1(const void* base, int64_t i) {
@@ -691,10 +709,7 @@ struct AdamChunk {
 };
 
 __device__ __forceinline__ void store_bf16x4(uint16_t* pb, const f32x4 p) {
-  u32x2 o;
-  o.x = bf16x2_bits(p.x, p.y);
-  o.y = bf16x2_bits(p.z, p.w);
-  st2u(pb, o);
+  st2u_nt(pb, u32x2{bf16x2_bits(p.x, p.y), bf16x2_bits(p.z, p.w)});
 }
 
 // Any chunk: runtime window division, bounds checks, ragged tail.
@@ -707,9 +722,9 @@ __device__ void adamw_generic(const AdamChunk& c, const AdamScalars& k) {
       const int v = v0 + u * kBlock;
       if (v < nvec) {
         a[u] = ld4f(c.acc + 4 * v);
-        p[u] = ld4f(c.p + 4 * v);
-        m[u] = ld4f(c.m + 4 * v);
-        w[u] = ld4f(c.v + 4 * v);
+        p[u] = ld4f_nt(c.p + 4 * v);
+        m[u] = ld4f_nt(c.m + 4 * v);
+        w[u] = ld4f_nt(c.v + 4 * v);
       }
     }
 #pragma unroll
@@ -717,9 +732,9 @@ __device__ void adamw_generic(const AdamChunk& c, const AdamScalars& k) {
       const int v = v0 + u * kBlock;
       if (v < nvec) {
         adamw4<kNoDiv>(a[u], p[u], m[u], w[u], k);
-        st4f(c.p + 4 * v, p[u]);
-        st4f(c.m + 4 * v, m[u]);
-        st4f(c.v + 4 * v, w[u]);
+        st4f_nt(c.p + 4 * v, p[u]);
+        st4f_nt(c.m + 4 * v, m[u]);
+        st4f_nt(c.v + 4 * v, w[u]);
         if (c.pb) store_bf16x4(c.pb + 4 * v, p[u]);
       }
     }
@@ -748,17 +763,17 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
     for (int u = 0; u < kUnrollAdam; ++u) {
       const int v = v0 + u * kBlock;
       a[u] = ld4f(c.acc + 4 * v);
-      p[u] = ld4f(c.p + 4 * v);
-      m[u] = ld4f(c.m + 4 * v);
-      w[u] = ld4f(c.v + 4 * v);
+      p[u] = ld4f_nt(c.p + 4 * v);
+      m[u] = ld4f_nt(c.m + 4 * v);
+      w[u] = ld4f_nt(c.v + 4 * v);
     }
 #pragma unroll
     for (int u = 0; u < kUnrollAdam; ++u) {
       const int v = v0 + u * kBlock;
       adamw4<WM>(a[u], p[u], m[u], w[u], k);
-      st4f(c.p + 4 * v, p[u]);
-      st4f(c.m + 4 * v, m[u]);
-      st4f(c.v + 4 * v, w[u]);
+      st4f_nt(c.p + 4 * v, p[u]);
+      st4f_nt(c.m + 4 * v, m[u]);
+      st4f_nt(c.v + 4 * v, w[u]);
       if (BF16) store_bf16x4(c.pb + 4 * v, p[u]);
     }
   }
