@@ -8,6 +8,11 @@ gro_reduce_norm, gro_clip_adamw with the BF16 parameter copy.  Inputs
 (per-microbatch BF16 gradient buckets, FP32 master/m/v) are resident in HBM
 before timing starts.
 
+Steps run back to back, so one call may find operands that the previous call
+left in the 256 MB Infinity Cache.  The JSON line's "cold_cache" object
+repeats both step kinds with an untimed read of an unrelated 1 GiB buffer
+before every call and reports the calls' summed durations.
+
 Prints ONE JSON line.  See --help for options.
 """
 from __future__ import annotations
@@ -24,6 +29,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+SHAPES = {
+    "draft-67m": "4 layers hidden 1024, 16384x1024 embedding",
+    "draft-67m-tp2-half": "4 layers hidden 1024, 8192x1024 embedding, TP2 half share",
+    "dense-1b-fsdp8-shard": "one 1/8 FSDP flat shard of a 1.34B dense model",
+    "hybrid-moe-4000": "4000 tensors, lognormal sizes, 70% EP-local experts",
+    "dense-8b-share": "one 1e9-element FSDP shard of an 8B dense model",
+}
 KERNEL_SRC = os.path.join(ROOT, "gradient_reduction_optimizer_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_draft-67m.json")
 
@@ -38,6 +50,8 @@ def parse():
                     help="fraction of the workload's elements the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="size of the buffer read before every call in the cold-cache timing (0: skip it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the benchmark, run a plain device copy of this many MiB three times "
                          "(the calibration kernel for rocprofv3 byte counters)")
@@ -152,20 +166,36 @@ def main():
         e.record(stream)
         return e
 
-    def one_step(mode: str, ev: dict):
+    flush_buf = (torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda:0")
+                 if args.flush_mib else None)
+
+    def no_flush():
+        pass
+
+    def flush():
+        # An untimed read of an unrelated buffer much larger than the 256 MB
+        # Infinity Cache: the next call finds none of its operands cached and
+        # no dirty lines of its own to write back.
+        flush_buf.sum()
+
+    def one_step(mode: str, ev: dict, pre=no_flush):
         step_no[0] += 1
         if mode == "microbatch":
             for k in range(n):
+                pre()
                 e0 = ev_pair()
                 B.gro_accumulate(plan.handle, 0, nb, grads[k], acc, k, n, s)
                 ev["k_accumulate"].append((e0, ev_pair()))
         else:
+            pre()
             e0 = ev_pair()
             B.gro_accumulate_window(plan.handle, 0, nb, window_ptrs, n, acc, s)
             ev["k_accumulate_window"].append((e0, ev_pair()))
+        pre()
         e0 = ev_pair()
         B.gro_reduce_norm(plan.handle, acc, n, s)
         ev["k_norm_final"].append((e0, ev_pair()))
+        pre()
         e0 = ev_pair()
         B.gro_clip_adamw(plan.handle, acc, n, w.max_norm, w.hparams, step_no[0], mp, mm, vm, pb, s)
         ev["k_adamw"].append((e0, ev_pair()))
@@ -212,12 +242,39 @@ def main():
                              "frac": step_bytes / (ms * 1e6) / HBM_PEAK_GBS},
                 "final_norm": norm}
 
+    def time_cold(mode: str) -> dict:
+        """The same steps with the cache flushed before every call: the sum
+        of the calls' event durations, without launch gaps."""
+        ev = {"k_accumulate": [], "k_accumulate_window": [], "k_norm_final": [], "k_adamw": []}
+        for _ in range(2):
+            one_step(mode, {k: [] for k in ev}, pre=flush)
+        for _ in range(args.steps):
+            one_step(mode, ev, pre=flush)
+        torch.cuda.synchronize()
+        acc_name = "k_accumulate" if mode == "microbatch" else "k_accumulate_window"
+        launches = {acc_name: n if mode == "microbatch" else 1, "k_norm_final": 1, "k_adamw": 1}
+        if mode == "microbatch":
+            alg = {acc_name: (n * 2 * c_mix + (4 + 8 * (n - 1)) * N) / n, "k_adamw": 30 * N}
+        else:
+            alg = {acc_name: n * 2 * c_mix + 4 * N, "k_adamw": 30 * N}
+        kernels = {}
+        for k, cnt in launches.items():
+            kernels[k] = {"avg_ms": avg_ms(ev[k])}
+            if k in alg:
+                gbs = alg[k] / (kernels[k]["avg_ms"] * 1e6)
+                kernels[k].update(GBps=gbs, frac=gbs / HBM_PEAK_GBS)
+        step_ms = sum(kernels[k]["avg_ms"] * cnt for k, cnt in launches.items())
+        log(f"{mode} (cold cache): {step_ms:.3f} ms of calls per step, " +
+            ", ".join(f"{k} {v['avg_ms'] * 1e3:.1f} us" for k, v in kernels.items()))
+        return {"calls_ms_per_step": step_ms, "value": N / (step_ms * 1e-3) / 1e9, "kernels": kernels}
+
     mb = time_mode("microbatch")
     wnd = time_mode("window")
     dom = wnd["dominant"]
     achieved = wnd["kernels"][dom]["GBps"]
     out = {
-        "metric": "Gparam updates/s (67M BF16 step, 1 GPU)",
+        "metric": "Gparam updates/s (67M BF16 step, 1 GPU)" if w.name == "draft-67m"
+                  else f"Gparam updates/s ({w.name} step, 1 GPU)",
         "value": wnd["value"],
         "unit": "Gparam updates/s",
         "n_gpus": 1,
@@ -229,8 +286,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic: BF16 grads N(0,1e-2) per microbatch, FP32 master N(0,0.02), seeded",
-        "config": {"workload": f"{w.name}: 4 layers hidden 1024, 16384x1024 embedding, "
-                               f"{w.numel} params as this GPU's share, R={w.R} stacked TP slots, "
+        "config": {"workload": f"{w.name}: {SHAPES.get(w.name, 'synthetic parameter set')}, "
+                               f"{w.numel} params as this GPU's share, R={w.R} stacked rank slots, "
                                f"accumulation window {n} reduced by one gro_accumulate_window call "
                                f"(every microbatch's BF16 gradient buckets resident), global norm, "
                                f"clip {w.max_norm}, AdamW with BF16 parameter copy",
@@ -249,6 +306,11 @@ def main():
                             "kernels": mb["kernels"]},
         "context": {"pages_ms_per_update_67M": [3.255, 2.624], "hardware_of_pages": "not stated"},
     }
+    if flush_buf is not None:
+        out["cold_cache"] = {
+            "protocol": f"an untimed {args.flush_mib} MiB read of an unrelated buffer before every call; "
+                        "per-call HIP event durations summed over the step (no launch gaps)",
+            "window_call": time_cold("window"), "microbatch_call": time_cold("microbatch")}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_frac, log)
     if args.copy_probe_mib:
