@@ -2,9 +2,12 @@
 
     python -m gradient_reduction_optimizer_amd.profiling stats <kernel_stats.csv>
     python -m gradient_reduction_optimizer_amd.profiling traffic <fetch counter csv> <write counter csv> \\
-        <elements per launch json> > traffic.json
+        <copy bytes> > traffic.json
+    python -m gradient_reduction_optimizer_amd.profiling counters <counter csv>
 
 `stats` prints the per-kernel call count and average/total duration.
+`counters` prints, for each of this library's kernels, the average per
+dispatch of every counter in a counter_collection.csv.
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per
 launch for each kernel, scaled by the ratio of known to counted bytes of the
 plain copy kernel that ran in the same process (the calibration).
@@ -74,8 +77,26 @@ def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
     return res
 
 
+def counters(path: str) -> str:
+    vals = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        k = short_name(r["Kernel_Name"])
+        if k in OURS:
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for k in vals for c in vals[k]})
+    out = ["kernel | dispatches | " + " | ".join(names)]
+    for k in OURS:
+        if k in vals:
+            n = max(len(v) for v in vals[k].values())
+            out.append(f"{k} | {n} | " + " | ".join(
+                f"{sum(vals[k][c]) / len(vals[k][c]):.6g}" if vals[k][c] else "-" for c in names))
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(kernel_stats(sys.argv[2]))
+    elif sys.argv[1] == "counters":
+        print(counters(sys.argv[2]))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4])), indent=1))
