@@ -53,7 +53,7 @@ def test_full_size_parity(name):
     assert_parity(cmps, norms)
 
 
-@pytest.mark.parametrize("name", ["draft-67m", "dense-1b-fsdp8-shard"])
+@pytest.mark.parametrize("name", ["draft-67m", "dense-1b-fsdp8-shard", "hybrid-moe-4000"])
 def test_full_size_parity_window_call(name):
     """The one-call-per-window entry point at full size."""
     w = CASES[name]()

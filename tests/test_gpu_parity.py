@@ -132,6 +132,24 @@ def test_window_call_matches_oracle_and_microbatch_calls(R):
     assert [n[0] for n in na] == [n[0] for n in nb_]
 
 
+def test_window_call_longest_windows():
+    """The longest window one call takes (64 microbatches, one bucket per
+    launch), then windows of 5 and 17 (the double-buffered path), with BF16
+    and FP32 contributions mixed: oracle results, and the same bits as one
+    gro_accumulate per microbatch."""
+    w = ragged_workload(R=2, bucket_elems=30000, fp32_every=3)
+    windows = [64, 5, 17]
+    log(f"case window call windows {windows}")
+    ca, cmps, na = run_parity(w, windows, window_call=True, log=log)
+    assert_parity(cmps, na)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+    cb, _, nb_ = run_parity(w, windows, window_call=False, log=log)
+    for arr in ("acc", "master", "m", "v"):
+        assert torch.equal(getattr(ca.st, arr).view(torch.int32), getattr(cb.st, arr).view(torch.int32)), arr
+    assert [n[0] for n in na] == [n[0] for n in nb_]
+
+
 def test_window_call_tiny_and_many_buckets():
     for w in (synth.tiny(), synth.tiny(bucket_elems=4096)):
         log(f"case window call {w.name} cap={w.bucket_elems}")
