@@ -43,13 +43,16 @@ namespace {
 constexpr int kBlock = GRO_BLOCK;      // lanes per workgroup (waves of 64)
 constexpr int kWaves = kBlock / 64;
 #ifndef GRO_UNROLL_ADAMW
-#define GRO_UNROLL_ADAMW GRO_UNROLL
+// A full AdamW chunk in one sweep: 16 independent 16-byte loads per lane
+// (120 VGPRs, 4 waves per SIMD) beat 8 loads at 5 waves per SIMD.
+#define GRO_UNROLL_ADAMW 4
 #endif
 #ifndef GRO_ADAMW_MIN_BLOCKS
 #define GRO_ADAMW_MIN_BLOCKS 1
 #endif
 constexpr int kUnroll = GRO_UNROLL;    // 4-element vectors in flight per lane
 constexpr int kUnrollAdam = GRO_UNROLL_ADAMW;
+static_assert((kChunkElems / 4) % (kUnrollAdam * kBlock) == 0, "whole AdamW sweeps per chunk");
 constexpr int kFinalBlock = 1024;      // the norm's second stage
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
 static_assert(kChunkElems % (4 * kBlock) == 0, "chunks are whole workgroup tiles");
