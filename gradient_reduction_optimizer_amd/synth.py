@@ -204,7 +204,7 @@ def stream_seed(*ids: int) -> int:
     return int((int(state[0]) << 31) ^ int(state[1])) & ((1 << 63) - 1)
 
 
-_GRAD, _MASTER = 1, 2
+_GRAD, _MASTER, _BUCKET_GRAD, _BUCKET_MASTER = 1, 2, 3, 4
 
 
 def _normal(numel: int, sigma: float, seed: int, device):
@@ -237,6 +237,21 @@ def grad_contribution(w: Workload, tensor_index: int, micro: int, slot: int, dev
         return grad_bf16(w, tensor_index, micro, slot, device=device)
     seed = stream_seed(w.seed, _GRAD, tensor_index, micro, slot)
     return _normal(t.numel, w.sigma, seed, device)
+
+
+def bucket_grads_bf16(w: Workload, step: int, micro: int, bucket: int, slots: int, length: int,
+                      device="cpu"):
+    """BF16 contributions for a whole bucket at once, [slots, length]: for
+    workloads too large to draw tensor by tensor (the 1e9-element share).
+    float32 normals times sigma, rounded by torch's float->bfloat16 cast."""
+    import torch
+    seed = stream_seed(w.seed, _BUCKET_GRAD, step, micro, bucket)
+    return _normal(slots * length, w.sigma, seed, device).view(slots, length).to(torch.bfloat16)
+
+
+def bucket_master(w: Workload, bucket: int, length: int, device="cpu"):
+    """FP32 master weights ~ N(0, master_sigma) for a whole bucket (1-D)."""
+    return _normal(length, w.master_sigma, stream_seed(w.seed, _BUCKET_MASTER, bucket), device)
 
 
 def host_values(t) -> np.ndarray:
