@@ -216,6 +216,14 @@ def main():
             one_step(mode, ev)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        # Per-step spread: from one step's first event to the next step's
+        # (the last step ends at its AdamW end event).
+        first = ev["k_accumulate"][::n] if mode == "microbatch" else ev["k_accumulate_window"]
+        starts = [a for a, _ in first]
+        ends = starts[1:] + [ev["k_adamw"][-1][1]]
+        spans = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+        pct = lambda q: spans[min(len(spans) - 1, int(q * (len(spans) - 1) + 0.5))]
+        spread = {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)}
         norm, _, finite = B.gro_plan_get_norm(plan.handle)
         if not finite:
             raise RuntimeError("the benchmark's norm is not finite: the timed steps skipped the update")
@@ -237,7 +245,8 @@ def main():
         step_bytes = acc_launch * acc_launches + 30 * N
         dom = max((acc_name, "k_adamw"), key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
         log(f"{mode}: {ms:.3f} ms/step, " + ", ".join(f"{k} {v['avg_ms'] * 1e3:.1f} us" for k, v in kernels.items()))
-        return {"ms_per_step": ms, "value": N / (ms * 1e-3) / 1e9, "kernels": kernels, "dominant": dom,
+        return {"ms_per_step": ms, "step_ms_events": spread, "value": N / (ms * 1e-3) / 1e9,
+                "kernels": kernels, "dominant": dom,
                 "step_hbm": {"alg_bytes": step_bytes, "GBps": step_bytes / (ms * 1e6),
                              "frac": step_bytes / (ms * 1e6) / HBM_PEAK_GBS},
                 "final_norm": norm}
@@ -281,6 +290,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": wnd["ms_per_step"],
+        "step_ms_events": wnd["step_ms_events"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -300,7 +310,8 @@ def main():
         "final_norm": wnd["final_norm"],
         "microbatch_call": {"note": "the same step with one gro_accumulate per microbatch (one gradient "
                                     "bucket set reused per microbatch in a real loop); bit-identical results",
-                            "value": mb["value"], "ms_per_step": mb["ms_per_step"], "step_hbm": mb["step_hbm"],
+                            "value": mb["value"], "ms_per_step": mb["ms_per_step"],
+                            "step_ms_events": mb["step_ms_events"], "step_hbm": mb["step_hbm"],
                             "roofline_kernel": mb["dominant"],
                             "roofline_frac": mb["kernels"][mb["dominant"]]["GBps"] / HBM_PEAK_GBS,
                             "kernels": mb["kernels"]},

@@ -71,10 +71,11 @@ class Compare:
 class Case:
     """One workload run through both the GPU path and the oracle."""
 
-    def __init__(self, w: synth.Workload, device="cuda", R: Optional[int] = None):
+    def __init__(self, w: synth.Workload, device="cuda", R: Optional[int] = None, poison: bool = False):
         self.w = w
         self.R = w.R if R is None else R
         self.device = device
+        self.poison = poison
         self.plan = Plan(w.tensors, self.R, w.bucket_elems)
         self.owners = M.assign_owners(w.tensors, self.R)
         self.st = DeviceState(self.plan, device)
@@ -96,7 +97,41 @@ class Case:
             self.v_h[i] = np.zeros(w.tensors[i].numel, np.float32)
         self.bufs = self.st.grad_buffers()
         self.window_bufs = []
+        if poison:
+            self.poison_flat_gaps()
+            self.poison_grad_padding(self.bufs)
         torch.cuda.synchronize()
+
+    # ------------------------------------------------- poisoned padding
+    def flat_gaps(self):
+        """[lo, hi) ranges of the flat arrays that no bucket covers."""
+        spans = sorted((bk["flat_base"], bk["flat_base"] + bk["len"]) for bk in self.plan.buckets)
+        gaps, at = [], 0
+        for lo, hi in spans:
+            if lo > at:
+                gaps.append((at, lo))
+            at = max(at, hi)
+        if self.st.acc.numel() > at:
+            gaps.append((at, self.st.acc.numel()))
+        return gaps
+
+    def poison_flat_gaps(self):
+        for lo, hi in self.flat_gaps():
+            for arr in (self.st.acc, self.st.master, self.st.m, self.st.v):
+                arr[lo:hi].fill_(float("nan"))
+            self.st.p_bf16[lo:hi].fill_(float("nan"))
+
+    def poison_grad_padding(self, bufs):
+        """NaN in every bucket buffer element past the bucket's length."""
+        for b, bk in enumerate(self.plan.buckets):
+            bufs[b][:, bk["len"]:].fill_(float("nan"))
+
+    def flat_gaps_untouched(self) -> bool:
+        for lo, hi in self.flat_gaps():
+            for arr in (self.st.acc, self.st.master, self.st.m, self.st.v, self.st.p_bf16):
+                if not bool(torch.isnan(arr[lo:hi]).all()):
+                    return False
+        return True
 
     def draw(self, step: int, k: int):
         """Per-tensor per-slot BF16 gradients of microbatch k of step."""
@@ -133,6 +168,8 @@ class Case:
         accumulate the whole window in one call."""
         while len(self.window_bufs) < n:
             self.window_bufs.append(self.st.grad_buffers())
+            if self.poison:
+                self.poison_grad_padding(self.window_bufs[-1])
         for k in range(n):
             for i, g in enumerate(grads_per_micro[k]):
                 if g is not None:
@@ -178,11 +215,12 @@ class Case:
 
 def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[float] = None,
                fuse: bool = True, R: Optional[int] = None, bucket_order=None, window_call: bool = False,
-               log=print, zero_tensors=()):
+               log=print, zero_tensors=(), poison: bool = False):
     """Run len(windows) optimizer steps on both sides and compare after each.
     window_call: use gro_accumulate_window (one call per window) instead of
-    one gro_accumulate per microbatch."""
-    c = Case(w, R=R)
+    one gro_accumulate per microbatch.  poison: NaN in every padding element
+    of the flat arrays and the gradient buffers before the first step."""
+    c = Case(w, R=R, poison=poison)
     max_norm = w.max_norm if max_norm is None else max_norm
     cmps = {k: Compare(k) for k in ("acc", "master", "m", "v", "p_bf16")}
     norms = []

@@ -132,6 +132,21 @@ def test_window_call_matches_oracle_and_microbatch_calls(R):
     assert [n[0] for n in na] == [n[0] for n in nb_]
 
 
+@pytest.mark.parametrize("window_call", [False, True])
+def test_poisoned_padding_is_never_read_or_written(window_call):
+    """NaN in every padding element -- the gradient buffers past each
+    bucket's length, and the flat-array gaps between buckets -- changes no
+    result (the oracle never sees it) and is still there afterwards."""
+    w = ragged_workload(R=2, bucket_elems=30000, fp32_every=4)
+    log(f"case poisoned padding, window_call={window_call}")
+    c, cmps, norms = run_parity(w, [3, 1, 2], window_call=window_call, poison=True, log=log)
+    assert c.flat_gaps(), "the layout has no gaps to poison"
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+    assert c.flat_gaps_untouched()
+
+
 def test_window_call_longest_windows():
     """The longest window one call takes (64 microbatches, one bucket per
     launch), then windows of 5 and 17 (the double-buffered path), with BF16
