@@ -50,6 +50,18 @@ const BucketDev* dev_buckets(const gro_plan* p) {
 double* dev_partials(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.partial_off); }
 double* dev_scalars(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.scalar_off); }
 
+// One accumulator per window: a call that starts buckets [b0, b1) on
+// another accumulator than the one buckets outside that range are already
+// accumulating into is a bookkeeping error.
+int check_window_acc(const gro_plan* p, int32_t b0, int32_t b1, const float* d_acc) {
+  if (p->acc_ptr == nullptr || p->acc_ptr == d_acc) return GRO_OK;
+  const int32_t nb = int32_t(p->buckets.size());
+  for (int32_t b = 0; b < nb; ++b)
+    if ((b < b0 || b >= b1) && p->count[size_t(b)] > 0)
+      return set_error(GRO_E_STATE, "bucket %d of this window accumulates into another accumulator", b);
+  return GRO_OK;
+}
+
 void reset_window(gro_plan* p) {
   std::fill(p->count.begin(), p->count.end(), 0);
   std::fill(p->partials_ready.begin(), p->partials_ready.end(), 0);
@@ -116,6 +128,8 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
   }
   if (micro_index != 0 && p->acc_ptr != nullptr && p->acc_ptr != d_acc)
     return set_error(GRO_E_STATE, "a different accumulator than earlier in this window");
+  rc = check_window_acc(p, b0, b1, d_acc);
+  if (rc != GRO_OK) return rc;
 
   const bool fuse = window_size > 0 && micro_index == window_size - 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -171,6 +185,8 @@ extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const 
         return set_error(GRO_E_INVALID, "microbatch %d buffer of bucket %d is NULL or not 16-byte aligned",
                          k, b0 + j);
     }
+  rc = check_window_acc(p, b0, b1, d_acc);
+  if (rc != GRO_OK) return rc;
   // Buckets of one launch: n * buckets <= kMaxBucketsPerLaunch pointers.
   const int32_t per = kMaxBucketsPerLaunch / n;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -193,7 +193,10 @@ int gro_plan_bind(gro_plan* plan, void* d_workspace, uint64_t bytes, void* strea
  * microbatches this bucket has accumulated in the current window (0 restarts).
  * window_size > 0 announces the window length: on its last microbatch the
  * kernel also writes the chunks' norm partials (saving gro_reduce_norm a read
- * of acc); 0 = not known.  Gradient buffers are only read. */
+ * of acc); 0 = not known.  Gradient buffers are only read.  All buckets of
+ * one window accumulate into one d_acc: starting buckets on another
+ * accumulator while other buckets of the window are in progress is
+ * GRO_E_STATE (a window ends with gro_clip_adamw or a rebind). */
 int gro_accumulate(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
                    float* d_acc, int32_t micro_index, int32_t window_size, void* stream);
 
@@ -207,8 +210,9 @@ int gro_accumulate(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_
  * elements of memory for (8n - 4) bytes per element less traffic).
  * d_grad_buckets: host array of n*(b1-b0) device pointers, microbatch-major:
  * entry k*(b1-b0) + j is microbatch k's BF16 buffer [slots][slot_stride] of
- * bucket b0+j.  n >= 1.  Leaves these buckets with a complete window of n
- * (any earlier partial window of theirs is discarded). */
+ * bucket b0+j.  1 <= n <= 64.  Leaves these buckets with a complete window
+ * of n (any earlier partial window of theirs is discarded).  The same
+ * one-accumulator rule as gro_accumulate applies. */
 int gro_accumulate_window(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
                           int32_t n, float* d_acc, void* stream);
 

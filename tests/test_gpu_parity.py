@@ -339,4 +339,15 @@ def test_window_bookkeeping_errors():
     with pytest.raises(B.GroError) as e:      # the window was consumed
         B.gro_reduce_norm(h, acc, 2, s)
     assert e.value.kind == "state"
+    # one accumulator per window
+    assert nb >= 2
+    acc2 = torch.zeros_like(c.st.acc)
+    B.gro_accumulate(h, 0, 1, ptrs[:1], acc, 0, 1, s)
+    for call in (lambda: B.gro_accumulate(h, 1, nb, ptrs[1:], acc2.data_ptr(), 0, 1, s),
+                 lambda: B.gro_accumulate_window(h, 1, nb, ptrs[1:], 1, acc2.data_ptr(), s)):
+        with pytest.raises(B.GroError) as e:
+            call()
+        assert e.value.kind == "state"
+    B.gro_accumulate_window(h, 1, nb, ptrs[1:], 1, acc, s)
+    B.gro_reduce_norm(h, acc, 1, s)
     torch.cuda.synchronize()
