@@ -186,6 +186,18 @@ def pin_partial_contributions_sum_to_full_gradient(M):
         assert not np.all(np.abs(mean_reading - full) <= bound)
 
 
+def pin_rank_order(M):
+    """Contributions are added in rank order 0, 1, ..., R-1 (FP32 addition is
+    not associative): 1 + 2^-24 rounds to 1 (a tie, to even) and again with
+    the second 2^-24, while 2^-24 + 2^-24 + 1 is exactly 1 + 2^-23."""
+    rows = M.assign_owners([spec(0, (1,), "partial")], 3)
+    bits = lambda v: M.f32_to_bf16(np.array([v], dtype=np.float32))
+    s = M.reduce_contributions(rows[0], 3, [bits(1.0), bits(2.0 ** -24), bits(2.0 ** -24)])
+    assert s[0] == np.float32(1.0)
+    s = M.reduce_contributions(rows[0], 3, [bits(2.0 ** -24), bits(2.0 ** -24), bits(1.0)])
+    assert s[0] == np.float32(1.0 + 2.0 ** -23)
+
+
 def pin_redundant_compute_is_averaged(M):
     """Every TP rank computing the full gradient redundantly: Replicate
     recovers it exactly, a Partial-style sum would double it."""
@@ -291,6 +303,15 @@ def pin_clip(M):
         tn = torch.nn.utils.clip_grad_norm_([p], max_norm).item()
         assert abs(tn - norm) <= 1e-6 * norm
         assert rel_close(clipped, p.grad.numpy(), 1e-6, floor=rms(clipped))
+    # a tiny norm, where clip_grad_norm_'s 1e-6 in the denominator is
+    # visible in FP32 (norm ~ 1e-3: a relative 1e-3 change of the coefficient)
+    small = (g * np.float32(3e-4)).astype(np.float32)
+    sn, _ = M.global_norm([small])
+    coef, stepped = M.clip_coefficient(sn, 1e-4)
+    p = torch.nn.Parameter(torch.zeros(small.size, dtype=torch.float32))
+    p.grad = torch.from_numpy(small.copy())
+    torch.nn.utils.clip_grad_norm_([p], 1e-4)
+    assert rel_close(small * coef, p.grad.numpy(), 1e-6, floor=rms(small * coef))
     # below the threshold, and clipping off, leave g untouched
     coef, stepped = M.clip_coefficient(norm, norm + 1.0)
     assert coef == 1.0 and stepped
@@ -471,6 +492,21 @@ def pin_init_uniform(M):
     # the index is the unsharded one: shard r of length n starts at r*n
     full = M.init_uniform(9, 4, 0, np.arange(64), 0.1, 0.0)
     assert np.array_equal(M.init_uniform(9, 4, 32, np.arange(32), 0.1, 0.0), full[32:])
+    # element g takes the top 24 bits of word g % 4 of block g // 4, drawn
+    # here with numpy's Philox (key (seed, param_id); it steps its 256-bit
+    # counter by one before each block, so block b comes from counter b - 1,
+    # and block 0 from the all-ones counter)
+    g = np.array([0, 1, 2, 3, 4, 5, 6, 7, 401, 402, 403, 404, 99999], dtype=np.int64)
+    want = []
+    ones = 2 ** 64 - 1
+    for e in g:
+        blk = int(e) >> 2
+        ctr = [blk - 1, 0, 0, 0] if blk > 0 else [ones, ones, ones, ones]
+        bg = np.random.Philox(key=np.array([7, 11], dtype=np.uint64), counter=np.array(ctr, dtype=np.uint64))
+        word = int(bg.random_raw(4)[int(e) & 3])
+        want.append(np.float32(2.0) * (np.float32(word >> 40) * np.float32(2.0 ** -24)) - np.float32(1.0))
+    got = M.init_uniform(7, 11, 0, g, 1.0, 0.0)
+    assert np.array_equal(got, np.array(want, dtype=np.float32))
 
 
 PINS = [
@@ -479,6 +515,7 @@ PINS = [
     pin_identical_replicas_average_to_replica,
     pin_partial_contributions_sum_to_full_gradient,
     pin_redundant_compute_is_averaged,
+    pin_rank_order,
     pin_local_owners_left_alone,
     pin_windows,
     pin_norm,

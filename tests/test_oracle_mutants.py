@@ -168,6 +168,93 @@ def _init_ignores_shard_offset(seed, param_id, index_base, indices, bound, offse
     return _orig["init_uniform"](seed, param_id, 0, indices, bound, offset)
 
 
+def _clip_without_eps(norm, max_norm):
+    import math
+    if not math.isfinite(norm):
+        return F32(1), False
+    if not (max_norm > 0) or math.isinf(max_norm):
+        return F32(1), True
+    return F32(min(1.0, max_norm / norm)) if norm > 0 else F32(1), True
+
+
+def _v_unclipped(g, coef, p, m, v, sc, decayed):
+    gh = g * F32(coef)
+    p = p * (sc.decay if decayed else F32(1.0))
+    m = sc.beta1 * m + sc.one_minus_beta1 * gh
+    v = sc.beta2 * v + sc.one_minus_beta2 * (g * g)
+    d = np.sqrt(v) / sc.sqrt_bc2 + sc.eps
+    p = p - sc.step_size * (m / d)
+    return p, m, v, M.f32_to_bf16(p)
+
+
+def _eps_before_bias_correction(g, coef, p, m, v, sc, decayed):
+    gh = g * F32(coef)
+    p = p * (sc.decay if decayed else F32(1.0))
+    m = sc.beta1 * m + sc.one_minus_beta1 * gh
+    v = sc.beta2 * v + sc.one_minus_beta2 * (gh * gh)
+    d = (np.sqrt(v) + sc.eps) / sc.sqrt_bc2
+    p = p - sc.step_size * (m / d)
+    return p, m, v, M.f32_to_bf16(p)
+
+
+def _no_second_moment_correction(lr, beta1, beta2, eps, weight_decay, step):
+    sc = _orig["adamw_scalars"](lr, beta1, beta2, eps, weight_decay, step)
+    sc.sqrt_bc2 = F32(1.0)
+    return sc
+
+
+def _step_off_by_one(lr, beta1, beta2, eps, weight_decay, step):
+    return _orig["adamw_scalars"](lr, beta1, beta2, eps, weight_decay, step + 1)
+
+
+def _frozen_not_excluded(tensors, R):
+    import copy
+    thawed = []
+    for t in tensors:
+        t = copy.copy(t)
+        if getattr(t, "frozen", False):
+            t.frozen = False
+        thawed.append(t)
+    return _orig["assign_owners"](thawed, R)
+
+
+def _slots_summed_last_first(owner, R, slots):
+    s = M.as_f32(slots[owner.slots - 1])
+    for r in range(owner.slots - 2, -1, -1):
+        s = s + M.as_f32(slots[r])
+    if owner.owner == M.MEAN:
+        s = s / F32(R)
+    return s
+
+
+def _init_wrong_word(seed, param_id, index_base, indices, bound, offset):
+    b, o = F32(bound), F32(offset)
+    out = np.empty(len(indices), dtype=F32)
+    for j, i in enumerate(indices):
+        g = int(index_base) + int(i)
+        blk = M.philox4x64_10((g >> 2, 0, 0, 0), (seed, param_id))
+        u = F32(blk[(g + 1) & 3] >> 40) * F32(2.0 ** -24)
+        out[j] = o + (F32(2.0) * u - F32(1.0)) * b
+    return out
+
+
+def _init_low_bits(seed, param_id, index_base, indices, bound, offset):
+    b, o = F32(bound), F32(offset)
+    out = np.empty(len(indices), dtype=F32)
+    for j, i in enumerate(indices):
+        g = int(index_base) + int(i)
+        blk = M.philox4x64_10((g >> 2, 0, 0, 0), (seed, param_id))
+        u = F32(blk[g & 3] & 0xFFFFFF) * F32(2.0 ** -24)
+        out[j] = o + (F32(2.0) * u - F32(1.0)) * b
+    return out
+
+
+def _init_one_sided(seed, param_id, index_base, indices, bound, offset):
+    v = _orig["init_uniform"](seed, param_id, index_base, indices, bound, offset)
+    # offset + u * bound instead of offset + (2u - 1) * bound
+    return (F32(offset) + (v - F32(offset) + F32(bound)) / F32(2.0)).astype(F32)
+
+
 def _widen_wrong_shift(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)).view(F32)
 
@@ -200,6 +287,16 @@ MUTANTS = {
     "fp32_rounded_to_bf16": ("as_f32", _fp32_through_bf16),
     "philox_nine_rounds": ("philox4x64_10", _philox_nine_rounds),
     "init_ignores_shard_offset": ("init_uniform", _init_ignores_shard_offset),
+    "clip_without_eps": ("clip_coefficient", _clip_without_eps),
+    "v_from_unclipped_gradient": ("adamw_update", _v_unclipped),
+    "eps_before_bias_correction": ("adamw_update", _eps_before_bias_correction),
+    "no_second_moment_correction": ("adamw_scalars", _no_second_moment_correction),
+    "step_off_by_one": ("adamw_scalars", _step_off_by_one),
+    "frozen_not_excluded": ("assign_owners", _frozen_not_excluded),
+    "slots_summed_last_first": ("reduce_contributions", _slots_summed_last_first),
+    "init_wrong_word": ("init_uniform", _init_wrong_word),
+    "init_low_bits": ("init_uniform", _init_low_bits),
+    "init_one_sided": ("init_uniform", _init_one_sided),
 }
 
 
