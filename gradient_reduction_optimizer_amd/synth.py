@@ -62,6 +62,7 @@ class Workload:
     weight_decay: float = 0.01
     max_norm: float = 1.0
     master_sigma: float = 0.02
+    values: str = "normal"        # "subnormal": contributions are random subnormal patterns
 
     @property
     def numel(self) -> int:
@@ -225,6 +226,8 @@ def grad_bf16(w: Workload, tensor_index: int, micro: int, slot: int,
     import torch
     n = w.tensors[tensor_index].numel if numel is None else numel
     seed = stream_seed(w.seed, _GRAD, tensor_index, micro, slot)
+    if w.values == "subnormal":
+        return _subnormal(n, seed, torch.int16, device).view(torch.bfloat16)
     return _normal(n, w.sigma, seed, device).to(torch.bfloat16)
 
 
@@ -236,7 +239,23 @@ def grad_contribution(w: Workload, tensor_index: int, micro: int, slot: int, dev
     if not t.fp32_grad:
         return grad_bf16(w, tensor_index, micro, slot, device=device)
     seed = stream_seed(w.seed, _GRAD, tensor_index, micro, slot)
+    if w.values == "subnormal":
+        return _subnormal(t.numel, seed, torch.int32, device).view(torch.float32)
     return _normal(t.numel, w.sigma, seed, device)
+
+
+def _subnormal(numel: int, seed: int, itype, device):
+    """Random subnormal bit patterns (exponent field 0, random sign and
+    nonzero mantissa) as a signed-integer tensor of the format's width."""
+    import torch
+    rng = np.random.default_rng(seed)
+    if itype == torch.int16:      # BF16: 7 mantissa bits
+        bits = rng.integers(1, 1 << 7, size=numel, dtype=np.uint32) | (rng.integers(0, 2, size=numel, dtype=np.uint32) << 15)
+        arr = bits.astype(np.uint16).view(np.int16)
+    else:                         # FP32: 23 mantissa bits
+        bits = rng.integers(1, 1 << 23, size=numel, dtype=np.uint32) | (rng.integers(0, 2, size=numel, dtype=np.uint32) << 31)
+        arr = bits.view(np.int32)
+    return torch.from_numpy(arr.copy()).to(device)
 
 
 def bucket_grads_bf16(w: Workload, step: int, micro: int, bucket: int, slots: int, length: int,

@@ -84,7 +84,7 @@ def test_tiny_small_buckets_split_tensors():
         assert k.n_diff_bits == 0, str(k)
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16])
 def test_ragged_sizes_every_R(R):
     w = ragged_workload(R=R)
     log(f"case ragged R={R}")
@@ -92,6 +92,25 @@ def test_ragged_sizes_every_R(R):
     assert_parity(cmps, norms)
     for k in cmps.values():
         assert k.n_diff_bits == 0, str(k)
+
+
+@pytest.mark.parametrize("R", [2, 3])
+@pytest.mark.parametrize("window_call", [False, True])
+def test_subnormal_contributions(R, window_call):
+    """Subnormal BF16 and FP32 contributions: the kernels' FP32 arithmetic
+    keeps subnormals (no flush to zero), as the oracle's numpy does -- the
+    sums, means, accumulation, the FP64 norm and m come out bit-identical
+    (v underflows to zero on both sides)."""
+    w = ragged_workload(R=R, fp32_every=4)
+    w.values = "subnormal"
+    log(f"case subnormal contributions R={R} window_call={window_call}")
+    c, cmps, norms = run_parity(w, [2, 3], window_call=window_call, log=log)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+    tiny = (c.st.acc != 0) & (c.st.acc.abs() < torch.finfo(torch.float32).tiny)
+    assert int(tiny.sum()) > 1000
+    assert 0.0 < norms[-1][0] < 1e-30
 
 
 def test_more_than_64_buckets_per_call():
