@@ -119,7 +119,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only; --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path).", file=sys.stderr)
+              f"(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
 
