@@ -19,10 +19,11 @@
 // (the library is built without contraction), so results are reproducible
 // bit for bit.
 //
-// Workgroup placement is XCD-aware: chunk q always runs in a workgroup whose
-// index is congruent to q modulo 8, and the hardware deals workgroups to the
-// eight XCDs round-robin, so a chunk visits the same XCD (and its L2) in
-// every pass of a step.
+// Workgroup placement is XCD-aware: in the accumulate and norm passes chunk q
+// runs in a workgroup whose index is congruent to q modulo 8, and the
+// hardware deals workgroups to the eight XCDs round-robin, so a chunk visits
+// the same XCD (and its L2) in each of them.  AdamW walks the chunks in
+// reverse (see k_adamw).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
