@@ -11,7 +11,10 @@ before timing starts.
 Steps run back to back, so one call may find operands that the previous call
 left in the 256 MB Infinity Cache.  The JSON line's "cold_cache" object
 repeats both step kinds with an untimed read of an unrelated 1 GiB buffer
-before every call and reports the calls' summed durations.
+before every call and reports the calls' summed durations.  "attainable"
+gives, for each timed kernel, the bandwidth a probe with the same access
+pattern and trivial arithmetic reaches (libgro_probe.so), and the roofline
+its fraction of that.
 
 Prints ONE JSON line.  See --help for options.
 """
@@ -38,6 +41,7 @@ SHAPES = {
 }
 KERNEL_SRC = os.path.join(ROOT, "gradient_reduction_optimizer_amd", "csrc", "kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_draft-67m.json")
+PROBE_LIB = os.path.join(ROOT, "gradient_reduction_optimizer_amd", "libgro_probe.so")
 
 
 def parse():
@@ -52,6 +56,8 @@ def parse():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="size of the buffer read before every call in the cold-cache timing (0: skip it)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the streaming probes that measure what each kernel's access pattern can reach")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the benchmark, run a plain device copy of this many MiB three times "
                          "(the calibration kernel for rocprofv3 byte counters)")
@@ -75,6 +81,67 @@ def load_traffic(kernel: str):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def attainable(st, n_micro: int, c_mix: int, N: int, flush, stream, log, reps: int = 20):
+    """Bandwidth that each timed kernel's access pattern reaches on this
+    device: libgro_probe.so moves the same arrays with the same element
+    types, cache policy and chunking as the kernel but does trivial
+    arithmetic.  Runs after the timed steps and overwrites the optimizer
+    state arrays (which hold real optimizer-state values when it starts).
+    Back to back ("GBps") and with the cache flushed before every launch
+    ("GBps_cold").  None if the probe library is not built."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    V = ctypes.c_void_p
+    lib.gro_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int64, V, V, V, V, V, V, ctypes.c_int, V]
+    lib.gro_probe_stream.restype = ctypes.c_int
+    n = (int(st.acc.numel()) // 4096) * 4096
+    k = int(round(n_micro * c_mix / N))  # BF16 streams the window kernel reads per element
+    # Random values like the real inputs: all-zero data streams several per
+    # cent faster on this device, which would overstate the ceiling.
+    gen = torch.Generator(device=st.acc.device)
+    gen.manual_seed(12345)
+    g = [(torch.randn(n, generator=gen, device=st.acc.device) * 1e-2).to(torch.bfloat16)
+         for _ in range(max(1, min(k, 8)))]
+    gp = (V * len(g))(*[x.data_ptr() for x in g])
+    s = stream.cuda_stream
+    ptrs = [st.acc.data_ptr(), st.master.data_ptr(), st.m.data_ptr(), st.v.data_ptr(), st.p_bf16.data_ptr()]
+
+    def run(pattern, kk, nbytes, cold):
+        ev = []
+        for i in range(3 + reps):
+            if cold:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.gro_probe_stream(pattern, n, *ptrs, gp, kk, s)
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"gro_probe_stream({pattern}) returned {rc}")
+            if i >= 3:
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        return nbytes * n / (ms * 1e6)
+
+    shapes = {"k_adamw": (0, 0, 30), "k_accumulate": (2, 1, 10)}
+    if 1 <= k <= 8:
+        shapes["k_accumulate_window"] = (1, k, 2 * k + 4)
+    res = {"note": "same arrays, element types, cache policy and chunking as the kernel, trivial arithmetic, "
+                   "random data; k_accumulate is its later-microbatch shape (BF16 in, FP32 read and written)"}
+    for name, (pattern, kk, b) in shapes.items():
+        res[name] = {"GBps": run(pattern, kk, b, False)}
+        if flush is not None:
+            res[name]["GBps_cold"] = run(pattern, kk, b, True)
+        log(f"attainable {name}: " + ", ".join(f"{key} {val:.0f}" for key, val in res[name].items()))
+    del g
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, frac: float, log, windows: int = 4):
@@ -322,6 +389,18 @@ def main():
             "protocol": f"an untimed {args.flush_mib} MiB read of an unrelated buffer before every call; "
                         "per-call HIP event durations summed over the step (no launch gaps)",
             "window_call": time_cold("window"), "microbatch_call": time_cold("microbatch")}
+    if not args.no_probe:
+        att = attainable(st, n, c_mix, N, flush if flush_buf is not None else None, stream, log)
+        out["attainable"] = att
+        for kdict in ((out["kernels"], out["microbatch_call"]["kernels"]) if att else ()):
+            for name, kv in kdict.items():
+                if name in att and "GBps" in kv:
+                    kv["frac_of_attainable"] = kv["GBps"] / att[name]["GBps"]
+        if att and dom in att:
+            out["roofline"]["frac_of_attainable"] = achieved / att[dom]["GBps"]
+            if "cold_cache" in out and att[dom].get("GBps_cold"):
+                ck = out["cold_cache"]["window_call"]["kernels"][dom]
+                ck["frac_of_attainable"] = ck["GBps"] / att[dom]["GBps_cold"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_frac, log)
     if args.copy_probe_mib:

@@ -1,4 +1,5 @@
-"""Build libgro.so (the C-ABI library) in-tree for gfx950.
+"""Build libgro.so (the C-ABI library) and libgro_probe.so (streaming
+probes for the benchmark) in-tree for gfx950.
 
     python -m gradient_reduction_optimizer_amd.build
 
@@ -18,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgro.so")
+PROBE_LIB = os.path.join(PKG, "libgro_probe.so")
 CLIENT = os.path.join(BUILD, "abi_client")
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -51,6 +53,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # Streaming probes (measurement only; bench.py reports what the kernels'
+    # access patterns can reach): a separate library, not part of the ABI.
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *COMMON, *HIP_FLAGS, "-shared", os.path.join(CSRC, "stream_probe.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     # A plain C client of the ABI (used by the tests): C compiler, HIP
     # runtime headers and library, linked against libgro.so.
     client = os.path.join(ROOT, "tests", "native", "abi_client.c")

@@ -71,6 +71,12 @@ def test_counter_averages_per_kernel(tmp_path):
     assert len(lines) == 2
 
 
+def test_probe_library_exports_its_entry_point():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "gradient_reduction_optimizer_amd", "libgro_probe.so"))
+    assert hasattr(lib, "gro_probe_stream")
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
