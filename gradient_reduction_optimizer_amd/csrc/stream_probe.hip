@@ -17,9 +17,10 @@
 //                           stream; write the FP32 stream.  10 bytes per
 //                           element.
 //
-// Arguments: n elements (a multiple of 4,096), device pointers as the pattern
-// needs them (unused ones may be NULL), `k` BF16 stream pointers in `g` for
-// pattern 1 (1 <= k <= 8).  Returns 0, -1 for bad arguments, or a hipError_t.
+// Arguments: n elements (a multiple of 4,096); device pointers as the pattern
+// needs them (unused ones may be NULL); for pattern 1, `k` BF16 stream
+// pointers in `g`, k in 1..8, 12 or 16 (the window kernel reads window length
+// x slots streams).  Returns 0, -1 for bad arguments, or a hipError_t.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,7 +49,7 @@ struct Streams {
   float* m;
   float* v;
   uint16_t* pb;
-  const uint16_t* g[8];
+  const uint16_t* g[16];
   int k;
 };
 
@@ -140,7 +141,7 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
       hipLaunchKernelGGL(probe_adamw, grid, block, 0, st, s, chunks);
       break;
     case 1:
-      if (!p || !g || k < 1 || k > 8) return -1;
+      if (!p || !g || k < 1 || k > 16) return -1;
       for (int j = 0; j < k; ++j) {
         if (!g[j]) return -1;
         s.g[j] = g[j];
@@ -153,7 +154,10 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
         case 5: hipLaunchKernelGGL(probe_window<5>, grid, block, 0, st, s); break;
         case 6: hipLaunchKernelGGL(probe_window<6>, grid, block, 0, st, s); break;
         case 7: hipLaunchKernelGGL(probe_window<7>, grid, block, 0, st, s); break;
-        default: hipLaunchKernelGGL(probe_window<8>, grid, block, 0, st, s); break;
+        case 8: hipLaunchKernelGGL(probe_window<8>, grid, block, 0, st, s); break;
+        case 12: hipLaunchKernelGGL(probe_window<12>, grid, block, 0, st, s); break;
+        case 16: hipLaunchKernelGGL(probe_window<16>, grid, block, 0, st, s); break;
+        default: return -1;
       }
       break;
     case 2:

@@ -59,6 +59,7 @@ def test_probe_rejects_bad_arguments(lib):
     g = torch.zeros(8192, dtype=torch.bfloat16, device="cuda")
     gp = (V * 1)(g.data_ptr())
     assert lib.gro_probe_stream(1, 4000, None, out.data_ptr(), None, None, None, gp, 1, s) == -1  # not whole chunks
-    assert lib.gro_probe_stream(1, 8192, None, out.data_ptr(), None, None, None, gp, 9, s) == -1  # k > 8
+    assert lib.gro_probe_stream(1, 8192, None, out.data_ptr(), None, None, None, gp, 9, s) == -1  # k not built
+    assert lib.gro_probe_stream(1, 8192, None, out.data_ptr(), None, None, None, gp, 17, s) == -1
     assert lib.gro_probe_stream(0, 8192, None, out.data_ptr(), None, None, None, None, 0, s) == -1  # missing arrays
     assert lib.gro_probe_stream(7, 8192, None, out.data_ptr(), None, None, None, gp, 1, s) == -1  # no such pattern
