@@ -215,16 +215,19 @@ class Case:
 
 def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[float] = None,
                fuse: bool = True, R: Optional[int] = None, bucket_order=None, window_call: bool = False,
-               log=print, zero_tensors=(), poison: bool = False):
+               log=print, zero_tensors=(), poison: bool = False, step_numbers: Optional[Sequence[int]] = None):
     """Run len(windows) optimizer steps on both sides and compare after each.
     window_call: use gro_accumulate_window (one call per window) instead of
     one gro_accumulate per microbatch.  poison: NaN in every padding element
-    of the flat arrays and the gradient buffers before the first step."""
+    of the flat arrays and the gradient buffers before the first step.
+    step_numbers: the optimizer step count t of each window (default 1, 2, ...)."""
     c = Case(w, R=R, poison=poison)
     max_norm = w.max_norm if max_norm is None else max_norm
     cmps = {k: Compare(k) for k in ("acc", "master", "m", "v", "p_bf16")}
     norms = []
-    for step, n in enumerate(windows, start=1):
+    steps = list(step_numbers) if step_numbers is not None else list(range(1, len(windows) + 1))
+    assert len(steps) == len(windows)
+    for step, n in zip(steps, windows):
         grads_host = []
         micro = []
         for k in range(n):

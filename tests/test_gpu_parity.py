@@ -113,6 +113,18 @@ def test_subnormal_contributions(R, window_call):
     assert 0.0 < norms[-1][0] < 1e-30
 
 
+def test_large_step_counts():
+    """Bias corrections at step counts from 1 to 2^40 (beta^t underflows to 0
+    long before): the FP64 host scalars and the kernels follow the oracle."""
+    w = ragged_workload(R=2)
+    steps = [1, 2, 1000, 10 ** 6, 2 ** 31 + 7, 2 ** 40]
+    log(f"case step counts {steps}")
+    _, cmps, norms = run_parity(w, [2] * len(steps), step_numbers=steps, log=log)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+
+
 def test_more_than_64_buckets_per_call():
     w = ragged_workload(bucket_elems=64, sizes=[5000, 3, 64, 129, 777])
     log("case ragged bucket_elems=64 (many launches per call)")
