@@ -109,13 +109,25 @@ def test_dense_8b_full_share_sampled(mode):
     acc, master, m, v and the BF16 copy are compared with the oracle, which
     takes the clip coefficient from a norm computed by torch (FP64) from
     those inputs -- the oracle cannot hold the full share in host memory;
-    the GPU norm is compared with that torch norm (within the FP32 tolerance:
-    torch divides by a non-power-of-two window as a multiply by the reciprocal); after the first window
-    every m and v element is checked against its closed form (m = (1-b1)g^,
-    v = (1-b2)g^2), and every BF16 copy against torch's cast of the master."""
-    w = synth.dense_8b_share()
-    windows = [8, 3]
-    log(f"case dense-8b-share full ({mode}): {w.numel} elements, windows {windows}")
+    the GPU norm is compared with that torch norm (within the FP32
+    tolerance: torch divides by a non-power-of-two window as a multiply by
+    the reciprocal); after the first window every m and v element is
+    checked against its closed form (m = (1-b1)g^, v = (1-b2)g^2), and every
+    BF16 copy against torch's cast of the master."""
+    _flat_share_sampled(synth.dense_8b_share(), [8, 3], mode)
+
+
+def test_flat_share_beyond_32_bit_offsets():
+    """One bucket of 2^31 + 2^20 + 3 elements (a ragged last chunk): element
+    offsets inside the bucket and in the flat arrays pass 2^31, so every
+    index computation must be 64-bit.  Same checks as the 8B share, windows
+    2 then 1; the sample includes both ends of the bucket."""
+    numel = 2 ** 31 + 2 ** 20 + 3
+    _flat_share_sampled(synth.dense_8b_share(numel=numel, bucket_elems=numel), [2, 1], "window")
+
+
+def _flat_share_sampled(w, windows, mode):
+    log(f"case {w.name} full ({mode}): {w.numel} elements, windows {windows}")
     plan = Plan(w.tensors, w.R, w.bucket_elems)
     st = DeviceState(plan, "cuda")
     s = torch.cuda.current_stream().cuda_stream
