@@ -227,3 +227,32 @@ def test_unbound_plan_calls_fail_before_device_work():
     with pytest.raises(B.GroError) as e:
         B.gro_plan_get_norm(plan.handle)
     assert e.value.kind == "state"
+
+
+def test_error_messages_are_per_thread():
+    """gro_last_error is thread-local: concurrent failing calls on distinct
+    threads each read back their own message; a successful call clears it."""
+    import threading
+    errors = {}
+    start = threading.Barrier(8)
+
+    def worker(i):
+        start.wait()
+        bad = [dict(param_id=i, shape=(4,), placement="shard", shard_index=100 + i)]
+        for _ in range(200):
+            with pytest.raises(B.GroError) as e:
+                B.gro_plan_create(bad, 2, 1 << 20)
+            if f"shard_index {100 + i}" not in str(e.value):
+                errors[i] = str(e.value)
+                return
+        h = B.gro_plan_create([dict(param_id=i, shape=(4,), placement="replicate", shard_index=-1)], 2, 1 << 20)
+        if B.gro_last_error() != "":
+            errors[i] = "not cleared: " + B.gro_last_error()
+        B.gro_plan_destroy(h)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
