@@ -382,3 +382,33 @@ def test_window_bookkeeping_errors():
     B.gro_accumulate_window(h, 1, nb, ptrs[1:], 1, acc, s)
     B.gro_reduce_norm(h, acc, 1, s)
     torch.cuda.synchronize()
+
+
+def test_two_plans_on_two_streams_from_two_threads():
+    """Distinct plans may be driven from distinct host threads on distinct
+    streams at the same time; both runs still match the oracle bit for bit."""
+    import threading
+    results, failures = {}, {}
+
+    def run(name, w, window_call):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                _, cmps, norms = run_parity(w, [3, 2, 4], window_call=window_call, log=lambda m: None)
+            torch.cuda.synchronize()
+            results[name] = (cmps, norms)
+        except Exception as e:  # surfaced below
+            failures[name] = repr(e)
+
+    ws = {"a": (ragged_workload(R=2, seed=21), False), "b": (ragged_workload(R=3, seed=22, fp32_every=3), True)}
+    threads = [threading.Thread(target=run, args=(k, w, wc)) for k, (w, wc) in ws.items()]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not failures, failures
+    for name, (cmps, norms) in results.items():
+        log(f"thread {name}: " + "; ".join(str(k) for k in cmps.values()))
+        assert_parity(cmps, norms)
+        for k in cmps.values():
+            assert k.n_diff_bits == 0, (name, str(k))
