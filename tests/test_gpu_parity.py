@@ -412,3 +412,46 @@ def test_two_plans_on_two_streams_from_two_threads():
         assert_parity(cmps, norms)
         for k in cmps.values():
             assert k.n_diff_bits == 0, (name, str(k))
+
+
+def test_rebinding_moves_the_tables_and_resets_the_window():
+    """gro_plan_bind may be repeated: the tables move to the new workspace,
+    an unfinished window is dropped (its bookkeeping reset), and results
+    equal a run that was bound there from the start.  A workspace that is
+    too small or misaligned is rejected."""
+    w = ragged_workload(R=2, bucket_elems=30000)
+    c = Case(w)
+    h, s = c.plan.handle, c.stream
+    nb = c.plan.info["n_buckets"]
+    ptrs = [b.data_ptr() for b in c.bufs]
+    need = int(c.plan.info["workspace_bytes"])
+    ws2 = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
+    base = (ws2.data_ptr() + 255) // 256 * 256
+    for bad_ptr, bad_bytes in ((base, need - 8), (base + 16, need)):
+        with pytest.raises(B.GroError) as e:
+            B.gro_plan_bind(h, bad_ptr, bad_bytes, s)
+        assert e.value.kind == "invalid"
+    B.gro_accumulate(h, 0, nb, ptrs, c.st.acc.data_ptr(), 0, 2, s)     # a window left unfinished
+    B.gro_plan_bind(h, base, need, s)
+    c.st.workspace_keepalive = ws2
+    with pytest.raises(B.GroError) as e:                                # its bookkeeping is gone
+        B.gro_reduce_norm(h, c.st.acc.data_ptr(), 2, s)
+    assert e.value.kind == "state"
+    with pytest.raises(B.GroError) as e:                                # and no norm is readable
+        B.gro_plan_get_norm(h)
+    assert e.value.kind == "state"
+    # full windows on the new workspace match the oracle
+    cmps = {k: Compare(k) for k in ("acc", "master", "m", "v", "p_bf16")}
+    for step, n in enumerate([2, 3], start=1):
+        grads_host = []
+        for k in range(n):
+            g = c.draw(step, k)
+            c.gpu_accumulate(g, k, n)
+            grads_host.append([None if x is None else [synth.host_values(t) for t in x] for x in g])
+        norm, _, finite = c.gpu_finish(n, step, w.max_norm)
+        res = c.oracle_window(grads_host, step, w.max_norm)
+        c.compare_acc(res, cmps["acc"])
+        c.compare_states(res, cmps)
+        assert finite and abs(norm - res.norm) <= FP32_RTOL * res.norm
+    for k in cmps.values():
+        assert k.ok and k.n_diff_bits == 0, str(k)
