@@ -83,10 +83,15 @@ _lib: Optional[ctypes.CDLL] = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libgro.so (raises if it is not built)."""
+    """Load libgro.so.  If the in-tree library has not been built yet and
+    hipcc is available, build it first; otherwise raise."""
     global _lib
     if _lib is not None:
         return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        if os.path.abspath(LIB_PATH) == os.path.abspath(_build.LIB) and os.path.exists(_build.HIPCC):
+            _build.build()
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gradient_reduction_optimizer_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
