@@ -248,8 +248,9 @@ def adamw_update(g: np.ndarray, coef, p: np.ndarray, m: np.ndarray, v: np.ndarra
     """Clip + AdamW (decoupled weight decay, bias-corrected) on one tensor.
 
     The pages name Adam/AdamW as the update (P1 "Preserved prototype and
-    evidence": "the next Adam update"; P4 "Optimizer and checkpoint
-    semantics": Adam and AdamW remain explicit options) without a formula;
+    evidence": the restored state matched the following Adam step; P4
+    "Optimizer and checkpoint semantics": Adam and AdamW remain explicit
+    options) without a formula;
     this is the standard decoupled form:
         g^ = g * coef
         p  = p * (1 - lr*wd)
