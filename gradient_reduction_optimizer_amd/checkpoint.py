@@ -13,8 +13,8 @@ and evidence" (restore from legacy ownership into native ownership exactly,
 then match the next Adam update) and section "Proposed scope and acceptance
 criteria" (checkpoint compatibility, exact restored state, continued
 updates); and Mixle "Distributed Transformer Training", section "Optimizer
-and checkpoint semantics" (a checkpoint is loadable only after its success
-manifest is written).
+and checkpoint semantics" (a save counts as complete, and may be loaded,
+once its success marker exists).
 
 Layout of a checkpoint directory:
     state.safetensors   master/<param_id>, m/<param_id>, v/<param_id> (FP32)

@@ -22,9 +22,9 @@
  * Mixle v0.8.1 "Distributed Transformer Training", section "Backend split":
  * a request that cannot be executed fails before fitting -- here every check
  * happens on the host before any device work, so a failed call has no side
- * effects.  Section "Optimizer and checkpoint semantics": optimizer routes are
- * keyed by stable logical parameter names -- here by a caller-chosen 64-bit
- * param_id.
+ * effects.  Section "Optimizer and checkpoint semantics": the optimizer
+ * addresses parameters by names that stay fixed across wrapping -- here a
+ * caller-chosen 64-bit param_id.
  *
  * One GPU holds the R rank contributions of a replicated parameter as R
  * stacked slots in its own HBM; the kernels do that GPU's share of the work.
@@ -246,9 +246,10 @@ int gro_clip_adamw(gro_plan* plan, const float* d_acc, int32_t window_size, doub
 /* Replica-consistent initialisation of the FP32 master shard (and the
  * optional BF16 copy) of every updated parameter, independent of the rank,
  * of the layout and of when it runs (NeMo Automodel issue #3857, section
- * "Why this needs separate work": parameters may be initialised after
- * parallelisation, and rank-specific training RNG must not become a common
- * initialisation RNG -- this draws nothing from any other generator).
+ * "Why this needs separate work": parameters can be created after the
+ * model is parallelised, and replicas must not rely on each rank's training
+ * random stream to start alike -- this draws nothing from any other
+ * generator).
  * Element i of parameter p gets offset_p + (2u - 1) * bound_p with u in
  * [0, 1) in steps of 2^-24, from Philox4x64-10 with key (seed, param_id)
  * and counter (g / 4, 0, 0, 0), word g % 4, top 24 bits, where g is the

@@ -22,7 +22,7 @@ import numpy as np
 F32 = np.float32
 
 # Owner classes.  One per parameter (P1, "Proposed scope and acceptance
-# criteria": exactly one gradient-reduction owner per parameter).
+# criteria": each parameter's gradient is reduced by a single owner).
 MEAN = "mean"                    # Replicate: complete gradients, averaged
 SUM = "sum"                      # Partial: partial contributions, summed
 LOCAL_SHARD = "local_shard"      # Shard: owned outright, never synchronised
