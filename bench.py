@@ -182,7 +182,22 @@ def cpu_baseline(w, frac: float, log, windows: int = 4):
             "sample": f"{len(pick)} of {len(w.tensors)} tensors ({total} of {w.numel} elements), "
                       f"{windows} optimizer steps of one {n}-microbatch window each (reduce, accumulate, "
                       f"norm, clip, AdamW), numpy single-threaded, {dt:.1f} s of oracle time",
-            "seconds": dt}
+            "seconds": dt, "host": _host_cpu()}
+
+
+def _host_cpu() -> dict:
+    """The host the oracle ran on: CPU model and the cores this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu": model, "cores_available": cores}
 
 
 def main():
