@@ -15,6 +15,9 @@
  *   per step, per microbatch, per tensor (not frozen), per slot: uint16 bf16[numel]
  * Output file: double norm[steps]; int32 finite[steps];
  *   per tensor (updated): float master[numel], m[numel], v[numel]; uint16 bf16[numel]
+ * With a third argument (a seed), the master read from the input is replaced
+ * by gro_init_uniform(seed, bound 0.02 for every tensor, offset 0) before
+ * the first window.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -32,7 +35,7 @@ static void rd(FILE* f, void* p, size_t n) { if (fread(p, 1, n, f) != n) DIE("sh
 static void wr(FILE* f, const void* p, size_t n) { if (fwrite(p, 1, n, f) != n) DIE("short write"); }
 
 int main(int argc, char** argv) {
-  if (argc != 3) DIE("usage: %s input output", argv[0]);
+  if (argc != 3 && argc != 4) DIE("usage: %s input output [init_seed]", argv[0]);
   FILE* in = fopen(argv[1], "rb");
   if (!in) DIE("cannot open %s", argv[1]);
   int32_t hdr[5];
@@ -85,6 +88,12 @@ int main(int argc, char** argv) {
     rd(in, h, (size_t)lay[i].numel * 4);
     HIPCHK(hipMemcpy(master + lay[i].flat_offset, h, (size_t)lay[i].numel * 4, hipMemcpyHostToDevice));
     free(h);
+  }
+  if (argc == 4) {
+    double* bounds = calloc((size_t)(nt > 0 ? nt : 1), sizeof(double));
+    for (int32_t i = 0; i < nt; ++i) bounds[i] = 0.02;
+    GROCHK(gro_init_uniform(plan, strtoull(argv[3], NULL, 10), bounds, NULL, master, NULL, s));
+    free(bounds);
   }
   /* one set of bucket buffers per microbatch of a window */
   const int nb = info.n_buckets;

@@ -23,8 +23,8 @@ def _workload():
     return w
 
 
-@pytest.mark.parametrize("use_window", [0, 1])
-def test_c_client_matches_oracle(tmp_path, gpu, use_window):
+@pytest.mark.parametrize("use_window,init_seed", [(0, None), (1, None), (1, 77)])
+def test_c_client_matches_oracle(tmp_path, gpu, use_window, init_seed):
     if not os.path.exists(CLIENT):
         pytest.fail(f"{CLIENT} is not built (run build())")
     w = _workload()
@@ -58,7 +58,14 @@ def test_c_client_matches_oracle(tmp_path, gpu, use_window):
             win.append(row)
         grads.append(win)
     f.close()
-    r = subprocess.run([CLIENT, str(tmp_path / "in.bin"), str(tmp_path / "out.bin")],
+    if init_seed is not None:
+        # the client replaces the master by gro_init_uniform(seed, bound 0.02)
+        for i, t in enumerate(w.tensors):
+            if i in master:
+                base = t.shard_index * t.numel if t.placement == "shard" else 0
+                master[i] = M.init_uniform(init_seed, t.param_id, base, np.arange(t.numel), 0.02, 0.0)
+    args = [CLIENT, str(tmp_path / "in.bin"), str(tmp_path / "out.bin")]
+    r = subprocess.run(args + ([str(init_seed)] if init_seed is not None else []),
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     print(r.stdout.strip(), flush=True)
