@@ -40,7 +40,7 @@ SHAPES = {
     "dense-8b-share": "one 1e9-element FSDP shard of an 8B dense model",
 }
 KERNEL_SRC = os.path.join(ROOT, "gradient_reduction_optimizer_amd", "csrc", "kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_draft-67m.json")
+PROFILES = os.path.join(ROOT, "profiles")  # traffic_<workload>.json: rocprofv3 byte counters
 PROBE_LIB = os.path.join(ROOT, "gradient_reduction_optimizer_amd", "libgro_probe.so")
 
 
@@ -73,7 +73,7 @@ def load_traffic(kernel: str, workload: str):
     """HBM traffic of `kernel` from the committed counter summary, or None if
     missing, taken on another workload or from a different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(PROFILES, f"traffic_{workload}.json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
