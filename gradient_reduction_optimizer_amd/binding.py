@@ -35,6 +35,7 @@ GRO_MAX_NDIM = 8
 
 EXPORTS = ("gro_plan_create", "gro_plan_destroy", "gro_plan_get_info", "gro_plan_tensor",
            "gro_plan_bucket", "gro_plan_bind", "gro_accumulate", "gro_accumulate_window",
+           "gro_accumulate_microbatches",
            "gro_reduce_norm", "gro_plan_get_norm", "gro_clip_adamw", "gro_init_uniform",
            "gro_last_error")
 
@@ -105,6 +106,7 @@ def load() -> ctypes.CDLL:
     L.gro_plan_bind.argtypes = [P, P, U64, P]
     L.gro_accumulate.argtypes = [P, I32, I32, ctypes.POINTER(P), P, I32, I32, P]
     L.gro_accumulate_window.argtypes = [P, I32, I32, ctypes.POINTER(P), I32, P, P]
+    L.gro_accumulate_microbatches.argtypes = [P, I32, I32, ctypes.POINTER(P), I32, I32, I32, P, P]
     L.gro_reduce_norm.argtypes = [P, P, I32, P]
     L.gro_plan_get_norm.argtypes = [P, ctypes.POINTER(D), ctypes.POINTER(D), ctypes.POINTER(I32)]
     L.gro_clip_adamw.argtypes = [P, P, I32, D, ctypes.POINTER(gro_adamw_hparams), I64, P, P, P, P, P]
@@ -205,6 +207,17 @@ def gro_accumulate_window(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[
     ptrs = (ctypes.c_void_p * m)(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
     _check(load().gro_accumulate_window(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, int(n),
                                         ctypes.c_void_p(d_acc), ctypes.c_void_p(stream)))
+
+
+def gro_accumulate_microbatches(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[int], first_micro: int,
+                                n: int, window_size: int, d_acc: int, stream: int = 0) -> None:
+    """Microbatches first_micro..first_micro+n-1 of a window; d_grad_buckets:
+    n*(b1-b0) pointers, microbatch-major."""
+    m = max(len(d_grad_buckets), 1)
+    ptrs = (ctypes.c_void_p * m)(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
+    _check(load().gro_accumulate_microbatches(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, int(first_micro),
+                                              int(n), int(window_size), ctypes.c_void_p(d_acc),
+                                              ctypes.c_void_p(stream)))
 
 
 def gro_reduce_norm(plan: int, d_acc: int, window_size: int, stream: int = 0) -> None:

@@ -162,17 +162,27 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
   return GRO_OK;
 }
 
-extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
-                                     int32_t n, float* d_acc, void* stream) {
-  clear_error();
+namespace {
+
+// Microbatches first_micro .. first_micro+n-1 of a window of window_size
+// (0 = length not known yet) for buckets [b0, b1), in one pass per bucket
+// run.  Shared by gro_accumulate_window (a whole window) and
+// gro_accumulate_microbatches (any group).
+int accumulate_group(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets, int32_t first_micro,
+                     int32_t n, int32_t window_size, float* d_acc, void* stream) {
   int rc = check_bound(p);
   if (rc != GRO_OK) return rc;
   const int32_t nb = int32_t(p->buckets.size());
   if (b0 < 0 || b1 < b0 || b1 > nb)
     return set_error(GRO_E_INVALID, "bucket range [%d, %d) not within [0, %d)", b0, b1, nb);
-  if (n < 1) return set_error(GRO_E_INVALID, "a window has at least one microbatch (n = %d)", n);
+  if (n < 1) return set_error(GRO_E_INVALID, "a group has at least one microbatch (n = %d)", n);
   if (n > kMaxBucketsPerLaunch)
-    return set_error(GRO_E_INVALID, "window of %d microbatches exceeds %d", n, kMaxBucketsPerLaunch);
+    return set_error(GRO_E_INVALID, "group of %d microbatches exceeds %d", n, kMaxBucketsPerLaunch);
+  if (first_micro < 0) return set_error(GRO_E_INVALID, "first_micro < 0");
+  if (window_size < 0) return set_error(GRO_E_INVALID, "window_size < 0");
+  if (window_size > 0 && int64_t(first_micro) + n > window_size)
+    return set_error(GRO_E_INVALID, "microbatches %d..%d outside a window of %d", first_micro, first_micro + n - 1,
+                     window_size);
   if (b1 == b0) return GRO_OK;
   if (d_grad_buckets == nullptr) return set_error(GRO_E_INVALID, "d_grad_buckets is NULL");
   if (d_acc == nullptr || !aligned16(d_acc))
@@ -183,10 +193,20 @@ extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const 
       const void* g = d_grad_buckets[int64_t(k) * span + j];
       if (g == nullptr || !aligned16(g))
         return set_error(GRO_E_INVALID, "microbatch %d buffer of bucket %d is NULL or not 16-byte aligned",
-                         k, b0 + j);
+                         first_micro + k, b0 + j);
     }
+  if (first_micro != 0) {
+    for (int32_t b = b0; b < b1; ++b)
+      if (p->count[size_t(b)] != first_micro)
+        return set_error(GRO_E_STATE, "bucket %d has accumulated %d microbatches, not %d", b, p->count[size_t(b)],
+                         first_micro);
+    if (p->acc_ptr != nullptr && p->acc_ptr != d_acc)
+      return set_error(GRO_E_STATE, "a different accumulator than earlier in this window");
+  }
   rc = check_window_acc(p, b0, b1, d_acc);
   if (rc != GRO_OK) return rc;
+
+  const bool fuse = window_size > 0 && first_micro + n == window_size;
   // Buckets of one launch: n * buckets <= kMaxBucketsPerLaunch pointers.
   const int32_t per = kMaxBucketsPerLaunch / n;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -202,6 +222,9 @@ extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const 
     a.n_buckets = le - lb;
     a.n_micro = n;
     a.R = p->R;
+    a.first = first_micro == 0 ? 1 : 0;
+    a.fuse_norm = fuse ? 1 : 0;
+    a.window = window_size;
     for (int32_t k = 0; k < n; ++k)
       for (int32_t b = lb; b < le; ++b)
         a.grads[k * (le - lb) + (b - lb)] = d_grad_buckets[int64_t(k) * span + (b - b0)];
@@ -211,12 +234,27 @@ extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const 
     if (e != hipSuccess) return hip_fail(e, "accumulate-window launch");
   }
   for (int32_t b = b0; b < b1; ++b) {
-    p->count[size_t(b)] = n;
-    p->partials_ready[size_t(b)] = 1;
+    p->count[size_t(b)] = first_micro + n;
+    p->partials_ready[size_t(b)] = fuse ? 1 : 0;
   }
   p->acc_ptr = d_acc;
   p->norm_done = false;
   return GRO_OK;
+}
+
+}  // namespace
+
+extern "C" int gro_accumulate_window(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
+                                     int32_t n, float* d_acc, void* stream) {
+  clear_error();
+  return accumulate_group(p, b0, b1, d_grad_buckets, 0, n, n, d_acc, stream);
+}
+
+extern "C" int gro_accumulate_microbatches(gro_plan* p, int32_t b0, int32_t b1,
+                                           const void* const* d_grad_buckets, int32_t first_micro, int32_t n,
+                                           int32_t window_size, float* d_acc, void* stream) {
+  clear_error();
+  return accumulate_group(p, b0, b1, d_grad_buckets, first_micro, n, window_size, d_acc, stream);
 }
 
 extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_size, void* stream) {

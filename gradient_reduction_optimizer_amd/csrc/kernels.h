@@ -35,8 +35,11 @@ struct WindowLaunch {
   int64_t q_begin, q_end;
   int32_t b_first;
   int32_t n_buckets;
-  int32_t n_micro;
+  int32_t n_micro;          // microbatches in this group
   int32_t R;
+  int32_t first;            // 1: the group opens the window (accumulator overwritten)
+  int32_t fuse_norm;        // 1: the group closes the window (norm partials written)
+  int32_t window;           // microbatches in the whole window (the norm's divisor)
   const void* grads[kMaxBucketsPerLaunch];
   float* acc;
   double* partials;

@@ -368,10 +368,12 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
 }
 
 // ------------------------------------------------- accumulate a window
-// The whole window in one pass: for every element, the n microbatches'
-// reductions are accumulated in registers in microbatch order (acc = red_0,
-// then acc = acc + red_k) -- the same operations as n accumulate passes --
-// and the accumulator is written once, with the norm partial.
+// Several microbatches of a window in one pass: for every element, the
+// group's reductions are accumulated in registers in microbatch order --
+// starting from red_0 when the group opens the window (`first`), else from
+// the accumulator in memory -- the same operations as one accumulate pass per
+// microbatch, and the accumulator is written once.  When the group closes the
+// window (`fuse`) the norm partial is written too.
 struct WinChunk {
   const WindowLaunch* P;
   int64_t off;         // chunk offset inside its bucket
@@ -381,6 +383,8 @@ struct WinChunk {
   int len;
   int slots;
   bool mean;
+  bool first;          // the group starts the window: overwrite the accumulator
+  bool fuse;           // the group ends the window: also sum (acc/window)^2
   Divisor rdiv;
   Divisor wdiv;
   __device__ const void* g(int k) const { return P->grads[k * P->n_buckets + j]; }
@@ -402,6 +406,7 @@ __device__ double window_generic(const WinChunk& c) {
   double ss = 0.0;
   for (int v = threadIdx.x; v < nvec; v += kBlock) {
     f32x4 acc;
+    if (!c.first) acc = ld4f(c.acc + 4 * v);
     for (int k = 0; k < n; ++k) {
       const void* g = c.g(k);
       f32x4 red = In::widen(In::load(g, c.off + 4 * v));
@@ -412,29 +417,32 @@ __device__ double window_generic(const WinChunk& c) {
         red.z = divide(red.z, c.rdiv);
         red.w = divide(red.w, c.rdiv);
       }
-      acc = k == 0 ? red : acc + red;
+      acc = (c.first && k == 0) ? red : acc + red;
     }
     st4f(c.acc + 4 * v, acc);
-    ss += sq(divide(acc.x, c.wdiv));
-    ss += sq(divide(acc.y, c.wdiv));
-    ss += sq(divide(acc.z, c.wdiv));
-    ss += sq(divide(acc.w, c.wdiv));
+    if (c.fuse) {
+      ss += sq(divide(acc.x, c.wdiv));
+      ss += sq(divide(acc.y, c.wdiv));
+      ss += sq(divide(acc.z, c.wdiv));
+      ss += sq(divide(acc.w, c.wdiv));
+    }
   }
   if ((c.len & 3) && int(threadIdx.x) == nvec % kBlock) {
     for (int i = nvec * 4; i < c.len; ++i) {
-      float a = win_reduce1<In>(c, 0, i);
+      float a = c.first ? win_reduce1<In>(c, 0, i) : c.acc[i] + win_reduce1<In>(c, 0, i);
       for (int k = 1; k < n; ++k) a = a + win_reduce1<In>(c, k, i);
       c.acc[i] = a;
-      ss += sq(divide(a, c.wdiv));
+      if (c.fuse) ss += sq(divide(a, c.wdiv));
     }
   }
   return ss;
 }
 
-// A full chunk with C slots, the MEAN divisor mode RM and the window
-// divisor mode WM fixed at compile time, any window length.  Microbatch
-// k+1's loads are issued before microbatch k's data is consumed.
-template <typename In, int C, int RM, int WM>
+// A full chunk with C slots, the MEAN divisor mode RM, the window divisor
+// mode WM (kNoDiv: no norm partial) and FIRST (the group opens the window)
+// fixed at compile time, any number of microbatches.  Microbatch k+1's loads
+// are issued before microbatch k's data is consumed.
+template <typename In, int C, int RM, int WM, bool FIRST>
 __device__ double window_full(const WinChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   const int n = c.P->n_micro;
@@ -446,9 +454,11 @@ __device__ double window_full(const WinChunk& c) {
     {
       const void* g = c.g(0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
         for (int r = 0; r < C; ++r) cur[u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
+        if (!FIRST) acc[u] = ld4f(c.acc + 4 * (v0 + u * kBlock));
+      }
     }
 #pragma unroll 1
     for (int k = 0; k < n; ++k) {
@@ -468,7 +478,7 @@ __device__ double window_full(const WinChunk& c) {
         red.y = divide_m<RM>(red.y, c.rdiv);
         red.z = divide_m<RM>(red.z, c.rdiv);
         red.w = divide_m<RM>(red.w, c.rdiv);
-        acc[u] = k == 0 ? red : acc[u] + red;
+        acc[u] = (FIRST && k == 0) ? red : acc[u] + red;
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
@@ -478,10 +488,12 @@ __device__ double window_full(const WinChunk& c) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       st4f(c.acc + 4 * (v0 + u * kBlock), acc[u]);
-      ss += sq(divide_m<WM>(acc[u].x, c.wdiv));
-      ss += sq(divide_m<WM>(acc[u].y, c.wdiv));
-      ss += sq(divide_m<WM>(acc[u].z, c.wdiv));
-      ss += sq(divide_m<WM>(acc[u].w, c.wdiv));
+      if (WM != kNoDiv) {
+        ss += sq(divide_m<WM>(acc[u].x, c.wdiv));
+        ss += sq(divide_m<WM>(acc[u].y, c.wdiv));
+        ss += sq(divide_m<WM>(acc[u].z, c.wdiv));
+        ss += sq(divide_m<WM>(acc[u].w, c.wdiv));
+      }
     }
   }
   return ss;
@@ -531,19 +543,23 @@ __device__ double window_full_n(const WinChunk& c) {
 template <typename In, int C, int RM, int WM>
 __device__ double window_full_w(const WinChunk& c) {
   // FP32 contributions take twice the registers: keep them double-buffered.
-  if (sizeof(typename In::raw_t) > 8) return window_full<In, C, RM, WM>(c);
+  if (sizeof(typename In::raw_t) > 8) return window_full<In, C, RM, WM, true>(c);
   switch (c.P->n_micro) {
     case 2: return window_full_n<In, C, RM, WM, 2>(c);
     case 3: return window_full_n<In, C, RM, WM, 3>(c);
     case 4: return window_full_n<In, C, RM, WM, 4>(c);
     case 8: return window_full_n<In, C, RM, WM, 8>(c);
-    default: return window_full<In, C, RM, WM>(c);
+    default: return window_full<In, C, RM, WM, true>(c);
   }
 }
 
 template <typename In, int C, int RM>
 __device__ double window_full_dispatch(const WinChunk& c) {
-  return c.wdiv.pow2 ? window_full_w<In, C, RM, kMulInv>(c) : window_full_w<In, C, RM, kIeeeDiv>(c);
+  if (c.first && c.fuse)  // a whole window in one pass
+    return c.wdiv.pow2 ? window_full_w<In, C, RM, kMulInv>(c) : window_full_w<In, C, RM, kIeeeDiv>(c);
+  // a group of microbatches inside a window
+  if (!c.fuse) return c.first ? window_full<In, C, RM, kNoDiv, true>(c) : window_full<In, C, RM, kNoDiv, false>(c);
+  return c.wdiv.pow2 ? window_full<In, C, RM, kMulInv, false>(c) : window_full<In, C, RM, kIeeeDiv, false>(c);
 }
 
 template <typename In>
@@ -568,11 +584,15 @@ __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch
   c.len = ch.len;
   c.slots = bk.slots;
   c.mean = bk.owner == GRO_OWNER_MEAN;
+  c.first = P.first != 0;
+  c.fuse = P.fuse_norm != 0;
   c.rdiv = make_divisor(P.R);
-  c.wdiv = make_divisor(P.n_micro);
+  c.wdiv = make_divisor(P.window > 0 ? P.window : 1);
   const double ss = bk.grad_fp32 ? window_chunk<F32In>(c) : window_chunk<Bf16In>(c);
-  const double t = block_sum(ss);
-  if (threadIdx.x == 0) P.partials[q] = t;
+  if (c.fuse) {
+    const double t = block_sum(ss);
+    if (threadIdx.x == 0) P.partials[q] = t;
+  }
 }
 
 // ------------------------------------------------------- norm, stage 1

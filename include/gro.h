@@ -216,6 +216,27 @@ int gro_accumulate(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_
 int gro_accumulate_window(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
                           int32_t n, float* d_acc, void* stream);
 
+/* Microbatches first_micro .. first_micro+n-1 of a window for buckets
+ * [b0, b1) in one pass: bit for bit what gro_accumulate with those
+ * micro_index values computes (starting from the accumulator in memory when
+ * first_micro > 0), with the accumulator read and written once for the
+ * group.  For callers that can keep a few microbatches' gradient buckets
+ * resident but not a whole window: n microbatches in g groups move
+ * 8 * (n - g) bytes per element less accumulator traffic than one call per
+ * microbatch (a window of 8 in groups of 4: 48 bytes per element).
+ * d_grad_buckets: host array of n*(b1-b0) device pointers, microbatch-major,
+ * as for gro_accumulate_window.  1 <= n <= 64, first_micro >= 0;
+ * first_micro > 0 requires every bucket in the range to have accumulated
+ * exactly first_micro microbatches of the current window into d_acc (else
+ * GRO_E_STATE).  window_size as for gro_accumulate (0 = not known; when
+ * first_micro + n == window_size the norm partials are written too;
+ * first_micro + n > window_size is GRO_E_INVALID).  gro_accumulate_window is
+ * this call with first_micro = 0 and window_size = n.  Calls of both kinds
+ * and gro_accumulate may be mixed within a window. */
+int gro_accumulate_microbatches(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
+                                int32_t first_micro, int32_t n, int32_t window_size, float* d_acc,
+                                void* stream);
+
 /* Global L2 norm of g = acc / window_size over every owned element, in FP64,
  * with no atomics: per-chunk partials summed in a fixed order, so the result
  * does not depend on launch shape and is bit-reproducible.  Every bucket must

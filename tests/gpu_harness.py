@@ -178,6 +178,27 @@ class Case:
         ptrs = [self.window_bufs[k][b].data_ptr() for k in range(n) for b in range(nb)]
         B.gro_accumulate_window(self.plan.handle, 0, nb, ptrs, n, self.st.acc.data_ptr(), self.stream)
 
+    def gpu_accumulate_groups(self, grads_per_micro, n: int, groups: Sequence[int], announce: bool = True):
+        """Pack the window's microbatches, then call gro_accumulate_microbatches
+        once per group (sizes `groups`, summing to n); `announce` passes the
+        window length (else 0, and gro_reduce_norm computes the partials)."""
+        assert sum(groups) == n
+        while len(self.window_bufs) < n:
+            self.window_bufs.append(self.st.grad_buffers())
+            if self.poison:
+                self.poison_grad_padding(self.window_bufs[-1])
+        for k in range(n):
+            for i, g in enumerate(grads_per_micro[k]):
+                if g is not None:
+                    self.st.pack(self.window_bufs[k], i, g)
+        nb = self.plan.info["n_buckets"]
+        k0 = 0
+        for g in groups:
+            ptrs = [self.window_bufs[k][b].data_ptr() for k in range(k0, k0 + g) for b in range(nb)]
+            B.gro_accumulate_microbatches(self.plan.handle, 0, nb, ptrs, k0, g, n if announce else 0,
+                                          self.st.acc.data_ptr(), self.stream)
+            k0 += g
+
     def gpu_finish(self, n: int, step: int, max_norm: float, with_bf16=True):
         B.gro_reduce_norm(self.plan.handle, self.st.acc.data_ptr(), n, self.stream)
         norm, norm_sq, finite = B.gro_plan_get_norm(self.plan.handle)
@@ -215,12 +236,15 @@ class Case:
 
 def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[float] = None,
                fuse: bool = True, R: Optional[int] = None, bucket_order=None, window_call: bool = False,
-               log=print, zero_tensors=(), poison: bool = False, step_numbers: Optional[Sequence[int]] = None):
+               log=print, zero_tensors=(), poison: bool = False, step_numbers: Optional[Sequence[int]] = None,
+               groups: Optional[Sequence[Sequence[int]]] = None, announce: bool = True):
     """Run len(windows) optimizer steps on both sides and compare after each.
     window_call: use gro_accumulate_window (one call per window) instead of
     one gro_accumulate per microbatch.  poison: NaN in every padding element
     of the flat arrays and the gradient buffers before the first step.
-    step_numbers: the optimizer step count t of each window (default 1, 2, ...)."""
+    step_numbers: the optimizer step count t of each window (default 1, 2, ...).
+    groups: per window, the group sizes for gro_accumulate_microbatches
+    (announce: pass the window length to it)."""
     c = Case(w, R=R, poison=poison)
     max_norm = w.max_norm if max_norm is None else max_norm
     cmps = {k: Compare(k) for k in ("acc", "master", "m", "v", "p_bf16")}
@@ -234,12 +258,14 @@ def run_parity(w: synth.Workload, windows: Sequence[int], max_norm: Optional[flo
             g = c.draw(step, k)
             for i in zero_tensors:  # an unused parameter: zero contributions
                 g[i] = [torch.zeros_like(x) for x in g[i]]
-            if window_call:
+            if window_call or groups is not None:
                 micro.append(g)
             else:
                 c.gpu_accumulate(g, k, n, fuse=fuse, bucket_order=bucket_order)
             grads_host.append([None if x is None else [synth.host_values(s) for s in x] for x in g])
-        if window_call:
+        if groups is not None:
+            c.gpu_accumulate_groups(micro, n, groups[len(norms)], announce=announce)
+        elif window_call:
             c.gpu_accumulate_window(micro, n)
         norm, norm_sq, finite = c.gpu_finish(n, step, max_norm)
         res = c.oracle_window(grads_host, step, max_norm)

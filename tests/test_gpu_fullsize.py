@@ -70,6 +70,17 @@ def test_full_size_parity_window_call(name):
     assert_parity(cmps, norms)
 
 
+@pytest.mark.parametrize("name,groups", [("draft-67m", [[2, 2]]), ("dense-1b-fsdp8-shard", [[4, 4], [2, 1]])])
+def test_full_size_parity_microbatch_groups(name, groups):
+    """gro_accumulate_microbatches in groups at full size."""
+    w = CASES[name]()
+    t0 = time.time()
+    log(f"case {name} (groups {groups}): {w.numel} elements, windows {w.windows}")
+    c, cmps, norms = run_parity(w, w.windows, groups=groups, log=log)
+    log(f"case {name} (groups) done in {time.time() - t0:.1f} s")
+    assert_parity(cmps, norms)
+
+
 # ------------------------------------------------ the whole 1e9-element share
 def _sample_positions(plan, n_random=20000, seed=11):
     """Positions in the single flat tensor to compare with the oracle:

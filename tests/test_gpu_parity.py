@@ -178,6 +178,63 @@ def test_poisoned_padding_is_never_read_or_written(window_call):
     assert c.flat_gaps_untouched()
 
 
+@pytest.mark.parametrize("R", [1, 2, 3])
+@pytest.mark.parametrize("announce", [True, False])
+def test_microbatch_groups_match_oracle_and_per_microbatch_calls(R, announce):
+    """gro_accumulate_microbatches over groups of a window (3+1+4 of 8, 2+1 of a
+    trailing 3, 5 of 5, 1 of 1), with and without the window length
+    announced: the oracle's results, and the same bits as one gro_accumulate
+    per microbatch."""
+    w = ragged_workload(R=R, bucket_elems=30000, fp32_every=4)
+    windows, groups = [8, 3, 5, 1], [[3, 1, 4], [2, 1], [5], [1]]
+    log(f"case microbatch groups R={R} announce={announce}")
+    ca, cmps, na = run_parity(w, windows, groups=groups, announce=announce, log=log)
+    assert_parity(cmps, na)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
+    cb, _, nb_ = run_parity(w, windows, log=log)
+    for arr in ("acc", "master", "m", "v"):
+        assert torch.equal(getattr(ca.st, arr).view(torch.int32), getattr(cb.st, arr).view(torch.int32)), arr
+    assert [n[0] for n in na] == [n[0] for n in nb_]
+
+
+def test_call_styles_mixed_within_one_window():
+    """One window of 6 built from gro_accumulate (microbatch 0), a group
+    (1-3), gro_accumulate (4) and a group of one that closes it (5) gives the
+    same bits as six gro_accumulate calls; a group that does not continue
+    where the buckets stand, or runs past the window, is rejected."""
+    w = ragged_workload(R=2, bucket_elems=30000)
+    ca, cb = Case(w), Case(w)
+    n = 6
+    micro = [ca.draw(1, k) for k in range(n)]
+    for k in range(n):
+        cb.gpu_accumulate(micro[k], k, n)
+    nb = ca.plan.info["n_buckets"]
+    while len(ca.window_bufs) < n:
+        ca.window_bufs.append(ca.st.grad_buffers())
+    for k in range(n):
+        for i, g in enumerate(micro[k]):
+            if g is not None:
+                ca.st.pack(ca.window_bufs[k], i, g)
+    h, s, acc = ca.plan.handle, ca.stream, ca.st.acc.data_ptr()
+    ptrs = lambda k0, g: [ca.window_bufs[k][b].data_ptr() for k in range(k0, k0 + g) for b in range(nb)]
+    B.gro_accumulate(h, 0, nb, [b.data_ptr() for b in ca.window_bufs[0]], acc, 0, n, s)
+    with pytest.raises(B.GroError) as e:                 # skips microbatch 1
+        B.gro_accumulate_microbatches(h, 0, nb, ptrs(2, 2), 2, 2, n, acc, s)
+    assert e.value.kind == "state"
+    with pytest.raises(B.GroError) as e:                 # runs past the window
+        B.gro_accumulate_microbatches(h, 0, nb, ptrs(1, 5) + ptrs(5, 1), 1, 6, n, acc, s)
+    assert e.value.kind == "invalid"
+    B.gro_accumulate_microbatches(h, 0, nb, ptrs(1, 3), 1, 3, n, acc, s)
+    B.gro_accumulate(h, 0, nb, [b.data_ptr() for b in ca.window_bufs[4]], acc, 4, n, s)
+    B.gro_accumulate_microbatches(h, 0, nb, ptrs(5, 1), 5, 1, n, acc, s)
+    na = ca.gpu_finish(n, 1, w.max_norm)
+    nb_ = cb.gpu_finish(n, 1, w.max_norm)
+    assert na[0] == nb_[0]
+    for arr in ("acc", "master", "m", "v"):
+        assert torch.equal(getattr(ca.st, arr).view(torch.int32), getattr(cb.st, arr).view(torch.int32)), arr
+
+
 def test_window_call_longest_windows():
     """The longest window one call takes (64 microbatches, one bucket per
     launch), then windows of 5 and 17 (the double-buffered path), with BF16

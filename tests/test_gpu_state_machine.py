@@ -58,14 +58,21 @@ class Model:
         return OK
 
     def window(self, b0, b1, n, acc):
-        if b0 < 0 or b1 < b0 or b1 > self.nb or n < 1 or n > 64:
+        return self.group(b0, b1, 0, n, n, acc)
+
+    def group(self, b0, b1, k0, n, W, acc):
+        if b0 < 0 or b1 < b0 or b1 > self.nb or n < 1 or n > 64 or k0 < 0 or W < 0 or (W > 0 and k0 + n > W):
             return INVALID
         if b1 == b0:
             return OK
+        if k0 != 0 and any(self.count[b] != k0 for b in range(b0, b1)):
+            return STATE
+        if k0 != 0 and self.acc is not None and self.acc != acc:
+            return STATE
         if self._other_active(b0, b1, acc):
             return STATE
         for b in range(b0, b1):
-            self.count[b] = n
+            self.count[b] = k0 + n
         self.acc, self.norm_done = acc, False
         return OK
 
@@ -117,7 +124,7 @@ def test_random_call_sequences_follow_the_documented_rules(gpu, seed):
     step = 1
     W_cur = 2
     for i in range(1000):
-        op = str(rng.choice(["acc", "acc", "acc", "win", "norm", "norm", "clip", "clip", "get", "bind"]))
+        op = str(rng.choice(["acc", "acc", "acc", "win", "grp", "grp", "norm", "norm", "clip", "clip", "get", "bind"]))
         a = int(rng.choice([0, 0, 0, 1]))                  # mostly the same accumulator
         acc = accs[a].data_ptr()
         W = int(rng.choice([1, 2, 3, 4]))
@@ -129,10 +136,10 @@ def test_random_call_sequences_follow_the_documented_rules(gpu, seed):
             elif all(c == W for c in model.count):
                 op = "norm"
             else:
-                op = "acc"
+                op = "acc" if rng.random() < 0.6 else "grp"
         if op == "clip" and rng.random() < 0.5:
             W_cur = int(rng.choice([1, 2, 3, 4]))
-        if op in ("acc", "win"):
+        if op in ("acc", "win", "grp"):
             b0 = int(rng.integers(-1, nb + 1)) if rng.random() < 0.05 else int(rng.integers(0, nb))
             b1 = b0 + int(rng.integers(0, nb - max(b0, 0) + 1)) if b0 >= 0 else nb
             if rng.random() < 0.1:
@@ -148,6 +155,17 @@ def test_random_call_sequences_follow_the_documented_rules(gpu, seed):
                 ptrs = [sets[0][min(max(b, 0), nb - 1)].data_ptr() for b in range(b0, b1)]
                 want = model.accumulate(b0, b1, k, W, a)
                 got = outcome(lambda: B.gro_accumulate(plan.handle, b0, b1, ptrs, acc, k, W, s))
+            elif op == "grp":
+                if W == W_cur and a == 0 and rng.random() < 0.7:
+                    b0, b1 = 0, nb
+                k0 = int(rng.choice([0, 1, 2, 3, -1])) if rng.random() < 0.2 else min(
+                    model.count[max(min(b0, nb - 1), 0)], W - 1)
+                n = int(rng.integers(1, 4)) if rng.random() < 0.9 else int(rng.choice([0, 65]))
+                Wg = W if rng.random() < 0.9 else 0
+                ptrs = [sets[(k0 + kk) % 4][min(max(b, 0), nb - 1)].data_ptr()
+                        for kk in range(n if 1 <= n <= 64 else 1) for b in range(b0, b1)]
+                want = model.group(b0, b1, k0, n, Wg, a)
+                got = outcome(lambda: B.gro_accumulate_microbatches(plan.handle, b0, b1, ptrs, k0, n, Wg, acc, s))
             else:
                 n = int(rng.choice([1, 2, 3, 4, 0, 65])) if rng.random() < 0.1 else W
                 ptrs = [sets[kk % 4][min(max(b, 0), nb - 1)].data_ptr() for kk in range(max(n, 0) if n <= 64 else 1)
@@ -181,5 +199,5 @@ def test_random_call_sequences_follow_the_documented_rules(gpu, seed):
     torch.cuda.synchronize()
     print(sorted(counts.items()))
     # the walk exercised both outcomes of the main calls
-    for op in ("acc", "norm", "clip"):
+    for op in ("acc", "grp", "norm", "clip"):
         assert counts.get((op, OK), 0) > 10 and counts.get((op, STATE), 0) > 10, (op, counts)
