@@ -1,8 +1,10 @@
 /*
  * A plain C client of the C ABI (include/gro.h): no Python, no torch.  It
  * allocates every device buffer with hipMalloc, reads a plan and its inputs
- * from a binary file, runs `steps` optimizer windows (one gro_accumulate per
- * microbatch, or one gro_accumulate_window per window), and writes the norm
+ * from a binary file, runs `steps` optimizer windows (use_window_call 0: one
+ * gro_accumulate per microbatch; 1: one gro_accumulate_window per window; 2:
+ * gro_accumulate_microbatches for the first half of each window, then for the
+ * rest), and writes the norm
  * of every window and the final master, m, v and BF16 copy to an output file.
  * tests/test_gpu_c_client.py writes the input, runs this program and checks
  * the output against the CPU oracle.
@@ -125,7 +127,14 @@ int main(int argc, char** argv) {
       }
       if (!use_window) GROCHK(gro_accumulate(plan, 0, nb, (const void* const*)&bufs[k * nb], acc, k, window, s));
     }
-    if (use_window) GROCHK(gro_accumulate_window(plan, 0, nb, (const void* const*)bufs, window, acc, s));
+    if (use_window == 1) GROCHK(gro_accumulate_window(plan, 0, nb, (const void* const*)bufs, window, acc, s));
+    if (use_window == 2) {
+      const int half = window / 2 > 0 ? window / 2 : 1;
+      GROCHK(gro_accumulate_microbatches(plan, 0, nb, (const void* const*)bufs, 0, half, window, acc, s));
+      if (window > half)
+        GROCHK(gro_accumulate_microbatches(plan, 0, nb, (const void* const*)&bufs[half * nb], half, window - half,
+                                           window, acc, s));
+    }
     GROCHK(gro_reduce_norm(plan, acc, window, s));
     GROCHK(gro_plan_get_norm(plan, &norms[t], NULL, &fin[t]));
     GROCHK(gro_clip_adamw(plan, acc, window, max_norm, &hp, (int64_t)t + 1, master, m, v, p16, s));
@@ -160,6 +169,7 @@ int main(int argc, char** argv) {
   HIPCHK(hipFree(p16));
   HIPCHK(hipStreamDestroy(s));
   gro_plan_destroy(plan);
-  printf("c client: %d steps of window %d, %s\n", steps, window, use_window ? "window call" : "per microbatch");
+  printf("c client: %d steps of window %d, %s\n", steps, window,
+         use_window == 1 ? "window call" : use_window == 2 ? "two groups" : "per microbatch");
   return 0;
 }

@@ -23,7 +23,7 @@ def _workload():
     return w
 
 
-@pytest.mark.parametrize("use_window,init_seed", [(0, None), (1, None), (1, 77)])
+@pytest.mark.parametrize("use_window,init_seed", [(0, None), (1, None), (2, None), (1, 77)])
 def test_c_client_matches_oracle(tmp_path, gpu, use_window, init_seed):
     if not os.path.exists(CLIENT):
         pytest.fail(f"{CLIENT} is not built (run build())")
