@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="size of the buffer read before every call in the cold-cache timing (0: skip it)")
+    ap.add_argument("--no-group", action="store_true",
+                    help="skip the group-call timing (gro_accumulate_microbatches over two groups)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the streaming probes that measure what each kernel's access pattern can reach")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -278,6 +280,12 @@ def main():
         if mode == "microbatch":
             for k in range(n):
                 call("k_accumulate", B.gro_accumulate, plan.handle, 0, nb, grads[k], acc, k, n, s)
+        elif mode == "group":
+            k0 = 0
+            for g in groups:
+                call("k_accumulate_group", B.gro_accumulate_microbatches, plan.handle, 0, nb,
+                     [p for k in range(k0, k0 + g) for p in grads[k]], k0, g, n, acc, s)
+                k0 += g
         else:
             call("k_accumulate_window", B.gro_accumulate_window, plan.handle, 0, nb, window_ptrs, n, acc, s)
         call("k_norm_final", B.gro_reduce_norm, plan.handle, acc, n, s)
@@ -297,7 +305,8 @@ def main():
         device synchronisations); HIP events recorded on the launch stream
         around every call of every sample_every-th of these steps give the
         per-kernel durations and the per-step spread."""
-        ev = {"k_accumulate": [], "k_accumulate_window": [], "k_norm_final": [], "k_adamw": []}
+        ev = {"k_accumulate": [], "k_accumulate_window": [], "k_accumulate_group": [], "k_norm_final": [],
+              "k_adamw": []}
         for _ in range(args.warmup):
             one_step(mode, None)
         torch.cuda.synchronize()
@@ -308,7 +317,8 @@ def main():
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
         # Per-step spread: each sampled step from its first call's start
         # event to its AdamW end event.
-        first = ev["k_accumulate"][::n] if mode == "microbatch" else ev["k_accumulate_window"]
+        first = (ev["k_accumulate"][::n] if mode == "microbatch" else
+                 ev["k_accumulate_group"][::len(groups)] if mode == "group" else ev["k_accumulate_window"])
         spans = sorted(a.elapsed_time(b[1]) for (a, _), b in zip(first, ev["k_adamw"]))
         pct = lambda q: spans[min(len(spans) - 1, int(q * (len(spans) - 1) + 0.5))]
         spread = {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9)}
@@ -319,6 +329,9 @@ def main():
         if mode == "microbatch":
             acc_launch = (n * 2 * c_mix + (4 + 8 * (n - 1)) * N) / n  # k=0: 2c+4, k>0: 2c+8 per element
             acc_name, acc_launches = "k_accumulate", n
+        elif mode == "group":                                          # first group 2cg+4, later 2cg+8
+            acc_launch = (n * 2 * c_mix + (4 + 8 * (len(groups) - 1)) * N) / len(groups)
+            acc_name, acc_launches = "k_accumulate_group", len(groups)
         else:
             acc_launch = n * 2 * c_mix + 4 * N                         # all n microbatches + one acc write
             acc_name, acc_launches = "k_accumulate_window", 1
@@ -365,7 +378,9 @@ def main():
             ", ".join(f"{k} {v['avg_ms'] * 1e3:.1f} us" for k, v in kernels.items()))
         return {"calls_ms_per_step": step_ms, "value": N / (step_ms * 1e-3) / 1e9, "kernels": kernels}
 
+    groups = [n // 2, n - n // 2] if n >= 2 else [n]
     mb = time_mode("microbatch")
+    grp = time_mode("group") if not args.no_group else None
     wnd = time_mode("window")
     dom = wnd["dominant"]
     achieved = wnd["kernels"][dom]["GBps"]
@@ -409,6 +424,12 @@ def main():
                             "roofline_kernel": mb["dominant"],
                             "roofline_frac": mb["kernels"][mb["dominant"]]["GBps"] / HBM_PEAK_GBS,
                             "kernels": mb["kernels"]},
+        "group_call": None if grp is None else {
+            "note": f"the same step with gro_accumulate_microbatches over groups {groups} of the window (only a "
+                    "group's buckets need to be resident); bit-identical results; k_accumulate_group is "
+                    "k_accumulate_window on a group",
+            "groups": groups, "value": grp["value"], "ms_per_step": grp["ms_per_step"],
+            "step_hbm": grp["step_hbm"], "kernels": grp["kernels"]},
         "context": {"pages_ms_per_update_67M": [3.255, 2.624], "hardware_of_pages": "not stated"},
     }
     if flush_buf is not None:
