@@ -512,3 +512,18 @@ def test_rebinding_moves_the_tables_and_resets_the_window():
         assert finite and abs(norm - res.norm) <= FP32_RTOL * res.norm
     for k in cmps.values():
         assert k.ok and k.n_diff_bits == 0, str(k)
+
+
+def test_two_hundred_steps_stay_bit_identical():
+    """A long run: 200 optimizer steps (windows of 1 to 4 microbatches, one
+    call per microbatch) on the literal tiny set; the states still match
+    the oracle bit for bit at every step, so nothing drifts as m and v grow
+    and the bias corrections approach 1."""
+    w = synth.tiny(literal=True)
+    rng = np.random.default_rng(5)
+    windows = [int(x) for x in rng.integers(1, 5, size=200)]
+    log(f"case 200 steps, {sum(windows)} microbatches")
+    _, cmps, norms = run_parity(w, windows, log=lambda m: None)
+    assert_parity(cmps, norms)
+    for k in cmps.values():
+        assert k.n_diff_bits == 0, str(k)
