@@ -161,14 +161,22 @@ typedef struct gro_adamw_hparams {
   double weight_decay;
 } gro_adamw_hparams;
 
-/* Build a plan: ownership of every tensor from its placement (one owner per
- * param_id; duplicates -> GRO_E_DUPLICATE; bad placement/shard_index/flags ->
- * GRO_E_PLACEMENT; R < 1, n_tensors < 0, ndim out of [0,8], negative dims,
- * bucket_elems < 64 -> GRO_E_INVALID), then the layout: tensors grouped by
- * (owner class, decay, gradient type) in the order MEAN, SUM, LOCAL_SHARD,
- * LOCAL_REDUCED (decayed first, BF16 first), descriptor order within a group, packed into buckets of at most
- * bucket_elems elements; only a tensor larger than the capacity is split.
- * Host only, deterministic.  On success *out owns the host tables. */
+/* Build a plan.  Passages: NeMo Automodel issue #3857, section "Why this
+ * needs separate work" (what a local gradient of a replicated parameter
+ * means, per placement) and section "Proposed scope and acceptance criteria"
+ * (explicit replica/partial/shard semantics, exactly one reduction owner,
+ * unsupported compositions rejected); NeMo AutoModel "Model Parallelizer
+ * API", section "Choose the Extension Point" (sharding units may be drawn as
+ * groups of one dtype -- here buckets hold one gradient type).
+ * First the ownership of every tensor from its placement, one owner per
+ * param_id: duplicates -> GRO_E_DUPLICATE; bad placement/shard_index/flags
+ * -> GRO_E_PLACEMENT; R < 1, n_tensors < 0, ndim out of [0,8], negative
+ * dims, bucket_elems < 64 -> GRO_E_INVALID.  Then the layout: tensors
+ * grouped by (owner class, decay, gradient type) in the order MEAN, SUM,
+ * LOCAL_SHARD, LOCAL_REDUCED (decayed first, BF16 first), descriptor order
+ * within a group, packed into buckets of at most bucket_elems elements; only
+ * a tensor larger than the capacity is split.  Host only, deterministic.  On
+ * success *out owns the host tables. */
 int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors, int32_t R,
                     int64_t bucket_elems, gro_plan** out);
 
@@ -184,7 +192,11 @@ int gro_plan_bucket(const gro_plan* plan, int32_t b, gro_bucket_info* out);
  * the copy.  Must precede the calls below; may be repeated (rebinding). */
 int gro_plan_bind(gro_plan* plan, void* d_workspace, uint64_t bytes, void* stream);
 
-/* Reduce + cast + accumulate one microbatch for buckets [b0, b1).
+/* Reduce + cast + accumulate one microbatch for buckets [b0, b1) -- NeMo
+ * Automodel issue #3857, section "Why this needs separate work" (Replicate
+ * contributions averaged, Partial summed, Shard and already-reduced used as
+ * they are) and section "Preserved prototype and evidence" (an FP32
+ * reduction hook on BF16 gradients, gradient accumulation).
  * d_grad_buckets: host array of b1-b0 device pointers; entry j is bucket
  * b0+j's BF16 gradient buffer [slots][slot_stride].  d_acc: FP32 [n_flat].
  * Per element: the slots are widened and summed in FP32 in slot order; MEAN
@@ -200,7 +212,10 @@ int gro_plan_bind(gro_plan* plan, void* d_workspace, uint64_t bytes, void* strea
 int gro_accumulate(gro_plan* plan, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
                    float* d_acc, int32_t micro_index, int32_t window_size, void* stream);
 
-/* The whole window of n microbatches for buckets [b0, b1) in one pass:
+/* The whole window of n microbatches for buckets [b0, b1) in one pass
+ * (NeMo Automodel issue #3857, section "Proposed scope and acceptance
+ * criteria": accumulation windows of one, several and a trailing number of
+ * microbatches; the reduction itself as for gro_accumulate):
  * bit for bit what gro_accumulate with micro_index 0..n-1 and window_size n
  * computes (per element: acc = red_0, then acc = acc + red_k in microbatch
  * order; norm partials written at the end), but the accumulator is written
@@ -217,8 +232,9 @@ int gro_accumulate_window(gro_plan* plan, int32_t b0, int32_t b1, const void* co
                           int32_t n, float* d_acc, void* stream);
 
 /* Microbatches first_micro .. first_micro+n-1 of a window for buckets
- * [b0, b1) in one pass: bit for bit what gro_accumulate with those
- * micro_index values computes (starting from the accumulator in memory when
+ * [b0, b1) in one pass (NeMo Automodel issue #3857, section "Preserved
+ * prototype and evidence": accumulation that includes partial windows):
+ * bit for bit what gro_accumulate with those micro_index values computes (starting from the accumulator in memory when
  * first_micro > 0), with the accumulator read and written once for the
  * group.  For callers that can keep a few microbatches' gradient buckets
  * resident but not a whole window: n microbatches in g groups move
@@ -237,8 +253,10 @@ int gro_accumulate_microbatches(gro_plan* plan, int32_t b0, int32_t b1, const vo
                                 int32_t first_micro, int32_t n, int32_t window_size, float* d_acc,
                                 void* stream);
 
-/* Global L2 norm of g = acc / window_size over every owned element, in FP64,
- * with no atomics: per-chunk partials summed in a fixed order, so the result
+/* Global L2 norm (NeMo Automodel issue #3857, section "Proposed scope and
+ * acceptance criteria": global norms checked against explicit references, no
+ * double reduction) of g = acc / window_size over every owned element, in
+ * FP64, with no atomics: per-chunk partials summed in a fixed order, so the result
  * does not depend on launch shape and is bit-reproducible.  Every bucket must
  * have accumulated exactly window_size microbatches (else GRO_E_STATE).  The
  * result stays on the device (read it with gro_plan_get_norm). */
@@ -252,7 +270,11 @@ int gro_reduce_norm(gro_plan* plan, const float* d_acc, int32_t window_size, voi
 int gro_plan_get_norm(gro_plan* plan, double* norm, double* norm_sq, int32_t* finite);
 
 /* Clip + fused AdamW on every updated element, after gro_reduce_norm of the
- * same window:
+ * same window (NeMo Automodel issue #3857, section "Preserved prototype and
+ * evidence": clipping and Adam updates on the owned state; section
+ * "Proposed scope and acceptance criteria": clipping on and off; Mixle
+ * "Distributed Transformer Training", section "Optimizer and checkpoint
+ * semantics": AdamW over parameters addressed by stable names):
  *   g = acc / window_size;  coef = min(1, max_norm / (norm + 1e-6)) in FP64
  *   rounded to FP32 when 0 < max_norm < inf, else 1 (clipping off);
  *   g^ = g*coef; p = p*(1 - lr*wd) (1 when GRO_NO_DECAY); m = b1*m + (1-b1)*g^;
