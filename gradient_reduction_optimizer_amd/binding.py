@@ -192,10 +192,32 @@ def gro_plan_bind(plan: int, d_workspace: int, nbytes: int, stream: int = 0) -> 
                                 ctypes.c_void_p(stream)))
 
 
+def _pointer_array(ptrs: Sequence[int], expected: int, what: str):
+    """A C array of the given device pointers.  `expected` is how many the
+    library will read (0 when it rejects the call's other arguments before
+    reading any); a list of another length must never reach it."""
+    if expected and len(ptrs) != expected:
+        raise ValueError(f"{what}: {len(ptrs)} pointers given, the call reads {expected}")
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*[ctypes.c_void_p(int(p)) for p in ptrs])
+
+
+# A window or group call takes at most this many microbatches (include/gro.h).
+GRO_MAX_GROUP = 64
+
+
+def _reads(plan: int, b0: int, b1: int, n: int = 1) -> int:
+    """Pointers the library reads for buckets [b0, b1) and n microbatches:
+    n * (b1 - b0) for a valid range and group size, else 0 (the library then
+    rejects the call, or does nothing, before reading a pointer)."""
+    nb = gro_plan_get_info(plan)["n_buckets"]
+    if not (0 <= int(b0) < int(b1) <= nb and 1 <= int(n) <= GRO_MAX_GROUP):
+        return 0
+    return int(n) * (int(b1) - int(b0))
+
+
 def gro_accumulate(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[int], d_acc: int,
                    micro_index: int, window_size: int = 0, stream: int = 0) -> None:
-    n = max(int(b1) - int(b0), 0)
-    ptrs = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
+    ptrs = _pointer_array(d_grad_buckets, _reads(plan, b0, b1), "gro_accumulate")
     _check(load().gro_accumulate(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, ctypes.c_void_p(d_acc),
                                  int(micro_index), int(window_size), ctypes.c_void_p(stream)))
 
@@ -203,8 +225,7 @@ def gro_accumulate(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[int], d
 def gro_accumulate_window(plan: int, b0: int, b1: int, d_grad_buckets: Sequence[int], n: int, d_acc: int,
                           stream: int = 0) -> None:
     """d_grad_buckets: n*(b1-b0) pointers, microbatch-major."""
-    m = max(len(d_grad_buckets), 1)
-    ptrs = (ctypes.c_void_p * m)(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
+    ptrs = _pointer_array(d_grad_buckets, _reads(plan, b0, b1, n), "gro_accumulate_window")
     _check(load().gro_accumulate_window(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, int(n),
                                         ctypes.c_void_p(d_acc), ctypes.c_void_p(stream)))
 
@@ -213,8 +234,7 @@ def gro_accumulate_microbatches(plan: int, b0: int, b1: int, d_grad_buckets: Seq
                                 n: int, window_size: int, d_acc: int, stream: int = 0) -> None:
     """Microbatches first_micro..first_micro+n-1 of a window; d_grad_buckets:
     n*(b1-b0) pointers, microbatch-major."""
-    m = max(len(d_grad_buckets), 1)
-    ptrs = (ctypes.c_void_p * m)(*[ctypes.c_void_p(int(p)) for p in d_grad_buckets])
+    ptrs = _pointer_array(d_grad_buckets, _reads(plan, b0, b1, n), "gro_accumulate_microbatches")
     _check(load().gro_accumulate_microbatches(ctypes.c_void_p(plan), int(b0), int(b1), ptrs, int(first_micro),
                                               int(n), int(window_size), ctypes.c_void_p(d_acc),
                                               ctypes.c_void_p(stream)))
@@ -244,8 +264,13 @@ def gro_clip_adamw(plan: int, d_acc: int, window_size: int, max_norm: float, hp:
 
 def gro_init_uniform(plan: int, seed: int, bounds: Sequence[float], offsets: Optional[Sequence[float]],
                      d_master: int, d_param_bf16: int = 0, stream: int = 0) -> None:
-    """bounds/offsets: one value per tensor, in descriptor order."""
-    n = max(len(bounds), 1)
+    """bounds/offsets: one value per tensor, in descriptor order (the library
+    reads the plan's n_tensors entries of each)."""
+    nt = gro_plan_get_info(plan)["n_tensors"]
+    if len(bounds) != nt or (offsets is not None and len(offsets) != nt):
+        raise ValueError(f"gro_init_uniform: bounds/offsets need {nt} entries each, got {len(bounds)}"
+                         f"{'' if offsets is None else ' / ' + str(len(offsets))}")
+    n = max(nt, 1)
     b = (ctypes.c_double * n)(*[float(x) for x in bounds])
     o = None if offsets is None else (ctypes.c_double * n)(*[float(x) for x in offsets])
     _check(load().gro_init_uniform(ctypes.c_void_p(plan), ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), b, o,

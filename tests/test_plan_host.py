@@ -256,3 +256,31 @@ def test_error_messages_are_per_thread():
     for t in threads:
         t.join()
     assert not errors, errors
+
+
+def test_binding_rejects_pointer_lists_of_the_wrong_length():
+    """The library reads n * (b1 - b0) gradient pointers from the host array
+    it is given; the binding refuses a list of any other length before the
+    call reaches it (a short list would be read past its end).  Only host
+    entry points run: the plan is never bound."""
+    w = synth.tiny()
+    plan = Plan(w.tensors, w.R, 4096)
+    nb = plan.info["n_buckets"]
+    assert nb >= 3
+    fake = [256 * (i + 1) for i in range(2 * nb)]
+    with pytest.raises(ValueError):
+        B.gro_accumulate(plan.handle, 0, nb, fake[:nb - 1], 256, 0, 1, 0)
+    with pytest.raises(ValueError):
+        B.gro_accumulate_window(plan.handle, 0, nb, fake[:nb], 2, 256, 0)
+    with pytest.raises(ValueError):
+        B.gro_accumulate_microbatches(plan.handle, 1, nb, fake[:nb], 0, 2, 2, 256, 0)
+    with pytest.raises(ValueError):
+        B.gro_init_uniform(plan.handle, 1, [0.1] * (len(w.tensors) - 1), None, 256, 0, 0)
+    with pytest.raises(ValueError):
+        B.gro_init_uniform(plan.handle, 1, [0.1] * len(w.tensors), [0.0] * 2, 256, 0, 0)
+    # arguments the library rejects on their own are passed through to it:
+    # it reports them before reading any pointer (here: the plan is unbound)
+    for call in (lambda: B.gro_accumulate_window(plan.handle, 0, nb, fake[:1], 65, 256, 0),
+                 lambda: B.gro_accumulate(plan.handle, 0, nb + 1, fake[:1], 256, 0, 1, 0)):
+        with pytest.raises(B.GroError):
+            call()
