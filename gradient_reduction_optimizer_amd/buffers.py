@@ -17,6 +17,8 @@ class Plan:
     def __init__(self, tensors: Sequence, R: int, bucket_elems: int):
         self.handle = B.gro_plan_create(tensors, R, bucket_elems)
         self.R = int(R)
+        # this rank's shard index per tensor, as registered (-1 unless Shard)
+        self.shard_index = [int(B._attr(t, "shard_index", -1)) for t in tensors]
         self.info = B.gro_plan_get_info(self.handle)
         self.tensors = [B.gro_plan_tensor(self.handle, i) for i in range(self.info["n_tensors"])]
         self.buckets = [B.gro_plan_bucket(self.handle, b) for b in range(self.info["n_buckets"])]
@@ -63,12 +65,12 @@ class DeviceState:
         self.m = torch.zeros(n, **f32)
         self.v = torch.zeros(n, **f32)
         self.p_bf16 = torch.zeros(n, dtype=torch.bfloat16, device=self.device) if with_bf16 else None
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         nbytes = int(plan.info["workspace_bytes"])
         self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
         base = self.workspace.data_ptr()
         self.ws_ptr = (base + 255) // 256 * 256
         self.ws_bytes = nbytes
-        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         B.gro_plan_bind(plan.handle, self.ws_ptr, nbytes, self.stream.cuda_stream)
 
     def grad_buffers(self) -> List:

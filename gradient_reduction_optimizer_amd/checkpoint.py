@@ -18,8 +18,13 @@ once its success marker exists).
 
 Layout of a checkpoint directory:
     state.safetensors   master/<param_id>, m/<param_id>, v/<param_id> (FP32)
-    meta.json           step, R, per-parameter shape/numel/owner/decayed
+    meta.json           step, R, per-parameter numel/owner/shard_index/decayed
     _SUCCESS            written last; its presence marks a complete save
+
+A rank-local shard's state belongs to that shard only: a parameter saved or
+restored as a Shard must be a Shard on both sides, with the same shard index
+and the same R (ownership may change freely among Replicate, Partial and
+already-reduced, whose state is the whole parameter's).
 
 This is host plumbing around the plan's layout (torch copies), not part of
 the per-step path.  The arrays may live on any torch device.
@@ -36,7 +41,7 @@ from . import binding as B
 MANIFEST = "_SUCCESS"
 STATE_FILE = "state.safetensors"
 META_FILE = "meta.json"
-FORMAT = "gro-owned-state-v1"
+FORMAT = "gro-owned-state-v2"
 
 
 class CheckpointError(RuntimeError):
@@ -66,7 +71,7 @@ def save_state(plan, master, m, v, step: int, directory: str) -> None:
         os.remove(manifest)
     tensors: Dict[str, "torch.Tensor"] = {}
     params = []
-    for row in plan.tensors:
+    for i, row in enumerate(plan.tensors):
         if not row["updated"]:
             continue
         pid = int(row["param_id"])
@@ -74,7 +79,7 @@ def save_state(plan, master, m, v, step: int, directory: str) -> None:
             tensors[f"{name}/{pid}"] = _slice(arr, row).detach().to("cpu", copy=True).contiguous() \
                 if row["numel"] else torch.zeros(0, dtype=torch.float32)
         params.append({"param_id": pid, "numel": int(row["numel"]), "owner": B.OWNER_NAMES[row["owner"]],
-                       "decayed": bool(row["decayed"])})
+                       "shard_index": int(plan.shard_index[i]), "decayed": bool(row["decayed"])})
     meta = {"format": FORMAT, "step": int(step), "R": int(plan.R), "params": params}
     for fname, writer in ((STATE_FILE, lambda p: save_file(tensors, p)),
                           (META_FILE, lambda p: open(p, "w").write(json.dumps(meta, indent=1)))):
@@ -107,12 +112,21 @@ def load_state(plan, master, m, v, directory: str) -> int:
     missing = [int(r["param_id"]) for r in plan.tensors if r["updated"] and int(r["param_id"]) not in saved]
     if missing:
         raise CheckpointError(f"checkpoint lacks updated parameters {missing[:8]}")
-    for row in plan.tensors:
+    shard = B.OWNER_NAMES[B.GRO_OWNER_LOCAL_SHARD]
+    for i, row in enumerate(plan.tensors):
         if not row["updated"]:
             continue
         pid = int(row["param_id"])
-        if saved[pid]["numel"] != row["numel"]:
-            raise CheckpointError(f"param_id {pid}: {saved[pid]['numel']} elements saved, plan has {row['numel']}")
+        sv = saved[pid]
+        if sv["numel"] != row["numel"]:
+            raise CheckpointError(f"param_id {pid}: {sv['numel']} elements saved, plan has {row['numel']}")
+        owner = B.OWNER_NAMES[row["owner"]]
+        if (sv["owner"] == shard) != (owner == shard):
+            raise CheckpointError(f"param_id {pid}: saved as {sv['owner']}, the plan owns it as {owner}; "
+                                  "a shard's state is not the whole parameter's")
+        if owner == shard and (sv["shard_index"] != plan.shard_index[i] or int(meta["R"]) != plan.R):
+            raise CheckpointError(f"param_id {pid}: shard {sv['shard_index']} of R={meta['R']} saved, "
+                                  f"the plan holds shard {plan.shard_index[i]} of R={plan.R}")
     for row in plan.tensors:
         if not row["updated"] or row["numel"] == 0:
             continue

@@ -97,3 +97,37 @@ def test_coverage_and_size_checks(tmp_path):
                             frozen=(i == 0)) for i, t in enumerate(w.tensors[:5])]
     f = Plan(fro, w.R, w.bucket_elems)
     assert load_state(f, *_states(f, 7), directory=str(tmp_path)) == 1
+
+
+def test_shard_state_restores_only_into_the_same_shard(tmp_path):
+    """A Shard parameter's state is that shard's: restoring it into a plan
+    that holds another shard index, another R, or the parameter as a
+    replicated tensor is refused; ownership changes among Replicate, Partial
+    and already-reduced stay allowed (the test above)."""
+    w = synth.tiny()
+    a = Plan(w.tensors, w.R, w.bucket_elems)
+    save_state(a, *_states(a, 8), step=4, directory=str(tmp_path))
+    shards = [i for i, t in enumerate(w.tensors) if t.placement == "shard"]
+    assert shards
+
+    def with_change(i, **kw):
+        t = w.tensors[i]
+        f = dict(placement=t.placement, shard_index=t.shard_index)
+        f.update(kw)
+        return [synth.TensorSpec(u.param_id, u.name, u.shape, f["placement"], shard_index=f["shard_index"])
+                if j == i else u for j, u in enumerate(w.tensors)]
+
+    i = shards[0]
+    other = (w.tensors[i].shard_index + 1) % w.R
+    for tensors, R in ((with_change(i, shard_index=other), w.R),
+                       (with_change(i, placement="replicate", shard_index=-1), w.R),
+                       (w.tensors, w.R + 1)):
+        p = Plan(tensors, R, w.bucket_elems)
+        with pytest.raises(CheckpointError):
+            load_state(p, *_states(p, 9), directory=str(tmp_path))
+    # a replicated tensor saved as such does not restore into a shard either
+    j = next(k for k, t in enumerate(w.tensors) if t.placement == "replicate")
+    b = Plan(with_change(j, placement="shard", shard_index=0), w.R, w.bucket_elems)
+    with pytest.raises(CheckpointError):
+        load_state(b, *_states(b, 10), directory=str(tmp_path))
+    assert load_state(a, *_states(a, 11), directory=str(tmp_path)) == 4
