@@ -49,6 +49,8 @@ const BucketDev* dev_buckets(const gro_plan* p) {
 }
 double* dev_partials(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.partial_off); }
 double* dev_scalars(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.scalar_off); }
+double* dev_groups(const gro_plan* p) { return reinterpret_cast<double*>(p->d_ws + p->ws.group_off); }
+uint32_t* dev_counters(const gro_plan* p) { return reinterpret_cast<uint32_t*>(p->d_ws + p->ws.counter_off); }
 
 // One accumulator per window: a call that starts buckets [b0, b1) on
 // another accumulator than the one buckets outside that range are already
@@ -72,18 +74,15 @@ void reset_window(gro_plan* p) {
 
 }  // namespace
 
-extern "C" int gro_plan_bind(gro_plan* p, void* d_workspace, uint64_t bytes, void* stream) {
-  clear_error();
-  if (p == nullptr || d_workspace == nullptr) return set_error(GRO_E_INVALID, "NULL argument");
-  if (reinterpret_cast<uintptr_t>(d_workspace) & 255u)
-    return set_error(GRO_E_INVALID, "workspace must be 256-byte aligned");
-  if (bytes < p->ws.total)
-    return set_error(GRO_E_INVALID, "workspace has %llu bytes, plan needs %llu",
-                     (unsigned long long)bytes, (unsigned long long)p->ws.total);
+namespace {
+
+// Upload the plan's tables into `ws` on `stream`, clear the norm's
+// completion counters (they must start at zero; every kernel that counts
+// returns them to zero), wait, and mark the plan bound there.
+int bind_to(gro_plan* p, char* ws, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(d_workspace);
-  hipError_t e = hipSuccess;
-  if (!p->bucket_dev.empty())
+  hipError_t e = hipMemsetAsync(ws + p->ws.counter_off, 0, p->ws.counter_bytes, s);
+  if (e == hipSuccess && !p->bucket_dev.empty())
     e = hipMemcpyAsync(ws + p->ws.bucket_off, p->bucket_dev.data(),
                        p->bucket_dev.size() * sizeof(BucketDev), hipMemcpyHostToDevice, s);
   if (e == hipSuccess && !p->chunks.empty())
@@ -100,6 +99,19 @@ extern "C" int gro_plan_bind(gro_plan* p, void* d_workspace, uint64_t bytes, voi
   p->norm_valid = false;
   reset_window(p);
   return GRO_OK;
+}
+
+}  // namespace
+
+extern "C" int gro_plan_bind(gro_plan* p, void* d_workspace, uint64_t bytes, void* stream) {
+  clear_error();
+  if (p == nullptr || d_workspace == nullptr) return set_error(GRO_E_INVALID, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(d_workspace) & 255u)
+    return set_error(GRO_E_INVALID, "workspace must be 256-byte aligned");
+  if (bytes < p->ws.total)
+    return set_error(GRO_E_INVALID, "workspace has %llu bytes, plan needs %llu",
+                     (unsigned long long)bytes, (unsigned long long)p->ws.total);
+  return bind_to(p, static_cast<char*>(d_workspace), stream);
 }
 
 extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets,
@@ -293,7 +305,13 @@ extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_s
     if (err != hipSuccess) return hip_fail(err, "norm stage-1 launch");
     b = e;
   }
-  const hipError_t err = launch_norm_final(dev_partials(p), int64_t(p->chunks.size()), dev_scalars(p), s);
+  NormFinalLaunch f;
+  f.partials = dev_partials(p);
+  f.n_chunks = int64_t(p->chunks.size());
+  f.group_sums = dev_groups(p);
+  f.counter = dev_counters(p);
+  f.scalars = dev_scalars(p);
+  const hipError_t err = launch_norm_final(f, s);
   if (err != hipSuccess) return hip_fail(err, "norm stage-2 launch");
   std::fill(p->partials_ready.begin(), p->partials_ready.end(), 1);
   p->norm_done = true;

@@ -53,6 +53,16 @@ struct NormLaunch {
   int32_t window;
 };
 
+// The norm's second stage: group sums of the chunk partials, then their
+// total, each in a fixed order.  `counter` is zero before and after.
+struct NormFinalLaunch {
+  const double* partials;
+  int64_t n_chunks;
+  double* group_sums;       // one per kNormGroup chunks
+  uint32_t* counter;
+  double* scalars;
+};
+
 struct AdamWLaunch {
   const ChunkDev* chunks;
   const BucketDev* buckets;
@@ -84,8 +94,7 @@ hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s);
 hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s);
 hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s);
 hipError_t launch_norm_partials(const NormLaunch& a, hipStream_t s);
-hipError_t launch_norm_final(const double* partials, int64_t n_chunks, double* scalars,
-                             hipStream_t s);
+hipError_t launch_norm_final(const NormFinalLaunch& a, hipStream_t s);
 hipError_t launch_adamw(const AdamWLaunch& a, hipStream_t s);
 
 }  // namespace gro

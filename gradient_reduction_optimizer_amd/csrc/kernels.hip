@@ -51,10 +51,24 @@ constexpr int kWaves = kBlock / 64;
 #ifndef GRO_ADAMW_MIN_BLOCKS
 #define GRO_ADAMW_MIN_BLOCKS 1
 #endif
+#ifndef GRO_UNROLL_ACC
+#define GRO_UNROLL_ACC GRO_UNROLL
+#endif
+#ifndef GRO_UNROLL_WIN
+#define GRO_UNROLL_WIN GRO_UNROLL
+#endif
+// Window lengths up to this many microbatches issue every microbatch's loads
+// at once (window_full_n); longer ones pipeline microbatch by microbatch.
+#ifndef GRO_WIN_ALL_AT_ONCE
+#define GRO_WIN_ALL_AT_ONCE 8
+#endif
 constexpr int kUnroll = GRO_UNROLL;    // 4-element vectors in flight per lane
+constexpr int kUnrollWin = GRO_UNROLL_WIN;  // the same for the full-chunk window paths
+static_assert((kChunkElems / 4) % (kUnrollWin * kBlock) == 0, "whole window sweeps per chunk");
+constexpr int kUnrollAcc = GRO_UNROLL_ACC;  // the same for the one-microbatch full-chunk pass
+static_assert((kChunkElems / 4) % (kUnrollAcc * kBlock) == 0, "whole accumulate sweeps per chunk");
 constexpr int kUnrollAdam = GRO_UNROLL_ADAMW;
 static_assert((kChunkElems / 4) % (kUnrollAdam * kBlock) == 0, "whole AdamW sweeps per chunk");
-constexpr int kFinalBlock = 1024;      // the norm's second stage
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole wave64s");
 static_assert(kChunkElems % (4 * kBlock) == 0, "chunks are whole workgroup tiles");
 
@@ -157,6 +171,18 @@ __device__ double block_sum(double x) {
 // Chunk index of this workgroup, placed so that q == blockIdx.x (mod 8).
 __device__ __forceinline__ int64_t chunk_of_block(int64_t q_begin) {
   return q_begin - (q_begin & 7) + int64_t(blockIdx.x);
+}
+
+// The window pass's chunk placement: 0 as chunk_of_block; 1 gives each of
+// the eight XCDs (workgroup index mod 8 under round-robin dispatch) one
+// contiguous eighth of the range.
+#ifndef GRO_WIN_MAP
+#define GRO_WIN_MAP 0
+#endif
+__device__ __forceinline__ int64_t window_chunk_of_block(int64_t q_begin, int64_t q_end) {
+  if (GRO_WIN_MAP == 0) return chunk_of_block(q_begin);
+  const int64_t per = (q_end - q_begin + 7) >> 3;
+  return q_begin + int64_t(blockIdx.x & 7) * per + int64_t(blockIdx.x >> 3);
 }
 
 __device__ __forceinline__ double sq(float x) {
@@ -284,14 +310,13 @@ __device__ double accumulate_generic(const AccChunk& c) {
 template <typename In, int C, int RM, bool FIRST, int WM>
 __device__ double accumulate_full(const AccChunk& c) {
   constexpr int nvec = kChunkElems / 4;
-  static_assert(nvec % (kUnroll * kBlock) == 0, "full chunks are whole rounds");
   double ss = 0.0;
 #pragma unroll 1
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    f32x4 red[kUnroll];
-    f32x4 old[kUnroll];
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnrollAcc * kBlock) {
+    f32x4 red[kUnrollAcc];
+    f32x4 old[kUnrollAcc];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollAcc; ++u) {
       const int v = v0 + u * kBlock;
       typename In::raw_t raw[C];
 #pragma unroll
@@ -302,7 +327,7 @@ __device__ double accumulate_full(const AccChunk& c) {
       for (int r = 1; r < C; ++r) red[u] = red[u] + In::widen(raw[r]);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollAcc; ++u) {
       const int v = v0 + u * kBlock;
       f32x4 s = red[u];
       s.x = divide_m<RM>(s.x, c.rdiv);
@@ -448,13 +473,13 @@ __device__ double window_full(const WinChunk& c) {
   const int n = c.P->n_micro;
   double ss = 0.0;
 #pragma unroll 1
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    f32x4 acc[kUnroll];
-    typename In::raw_t cur[kUnroll][C], nxt[kUnroll][C];
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnrollWin * kBlock) {
+    f32x4 acc[kUnrollWin];
+    typename In::raw_t cur[kUnrollWin][C], nxt[kUnrollWin][C];
     {
       const void* g = c.g(0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollWin; ++u) {
 #pragma unroll
         for (int r = 0; r < C; ++r) cur[u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
         if (!FIRST) acc[u] = ld4f(c.acc + 4 * (v0 + u * kBlock));
@@ -465,12 +490,12 @@ __device__ double window_full(const WinChunk& c) {
       if (k + 1 < n) {
         const void* g = c.g(k + 1);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kUnrollWin; ++u)
 #pragma unroll
           for (int r = 0; r < C; ++r) nxt[u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kUnrollWin; ++u) {
         f32x4 red = In::widen(cur[u][0]);
 #pragma unroll
         for (int r = 1; r < C; ++r) red = red + In::widen(cur[u][r]);
@@ -481,12 +506,12 @@ __device__ double window_full(const WinChunk& c) {
         acc[u] = (FIRST && k == 0) ? red : acc[u] + red;
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnrollWin; ++u)
 #pragma unroll
         for (int r = 0; r < C; ++r) cur[u][r] = nxt[u][r];
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollWin; ++u) {
       st4f(c.acc + 4 * (v0 + u * kBlock), acc[u]);
       if (WM != kNoDiv) {
         ss += sq(divide_m<WM>(acc[u].x, c.wdiv));
@@ -500,24 +525,24 @@ __device__ double window_full(const WinChunk& c) {
 }
 
 // Common window lengths: every microbatch's loads are issued before any
-// is consumed (N * C * kUnroll loads in flight per lane).
+// is consumed (N * C * kUnrollWin loads in flight per lane).
 template <typename In, int C, int RM, int WM, int N>
 __device__ double window_full_n(const WinChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   double ss = 0.0;
 #pragma unroll 1
-  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
-    typename In::raw_t raw[N][kUnroll][C];
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnrollWin * kBlock) {
+    typename In::raw_t raw[N][kUnrollWin][C];
 #pragma unroll
     for (int k = 0; k < N; ++k) {
       const void* g = c.g(k);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kUnrollWin; ++u)
 #pragma unroll
         for (int r = 0; r < C; ++r) raw[k][u][r] = In::load(g, int64_t(r) * c.stride + c.off + 4 * (v0 + u * kBlock));
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kUnrollWin; ++u) {
       f32x4 acc;
 #pragma unroll
       for (int k = 0; k < N; ++k) {
@@ -544,7 +569,9 @@ template <typename In, int C, int RM, int WM>
 __device__ double window_full_w(const WinChunk& c) {
   // FP32 contributions take twice the registers: keep them double-buffered.
   if (sizeof(typename In::raw_t) > 8) return window_full<In, C, RM, WM, true>(c);
-  switch (c.P->n_micro) {
+  const int n = c.P->n_micro;
+  if (n > GRO_WIN_ALL_AT_ONCE) return window_full<In, C, RM, WM, true>(c);
+  switch (n) {
     case 2: return window_full_n<In, C, RM, WM, 2>(c);
     case 3: return window_full_n<In, C, RM, WM, 3>(c);
     case 4: return window_full_n<In, C, RM, WM, 4>(c);
@@ -571,7 +598,7 @@ __device__ double window_chunk(const WinChunk& c) {
 }
 
 __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch P) {
-  const int64_t q = chunk_of_block(P.q_begin);
+  const int64_t q = window_chunk_of_block(P.q_begin, P.q_end);
   if (q < P.q_begin || q >= P.q_end) return;
   const ChunkDev ch = P.chunks[q];
   const BucketDev bk = P.buckets[ch.bucket];
@@ -663,33 +690,48 @@ __global__ __launch_bounds__(kBlock) void k_norm_partials(const NormLaunch P) {
 }
 
 // ------------------------------------------------------- norm, stage 2
-// One workgroup: lane t sums partials t, t+1024, ... in order, then a fixed
-// butterfly and the sixteen wave totals in order.  No atomics.
-__global__ __launch_bounds__(kFinalBlock) void k_norm_final(const double* __restrict__ partials,
-                                                            int64_t n, double* __restrict__ scalars) {
-  // Lane t adds partials t, t+1024, t+2048, ... in that order; the loads of
-  // eight consecutive terms are issued together so they overlap.
-  double s = 0.0;
-  int64_t i = threadIdx.x;
-  for (; i + 7 * kFinalBlock < n; i += 8 * kFinalBlock) {
-    double x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = partials[i + j * kFinalBlock];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += x[j];
+// Two fixed-order levels, so the result never depends on launch shape or on
+// which workgroup runs when:
+//   group sum j = the kNormGroup partials kNormGroup*j .. (one per lane, lane
+//                 t takes partial kNormGroup*j + t; butterfly, then the wave
+//                 totals in wave order);
+//   total       = the group sums (lane t adds sums t, t + kBlock, ... in that
+//                 order; butterfly; wave totals in order).
+// One workgroup per group.  The workgroup that finishes last -- found with a
+// completion counter, which it returns to zero -- adds the group sums and
+// writes the norm.  The counter only says who is last; no atomic operation
+// touches a sum.
+static_assert(kNormGroup == kBlock, "one partial per lane in a group sum");
+
+__device__ __forceinline__ void write_norm(double t, double* scalars) {
+  scalars[kNormSq] = t;
+  scalars[kNorm] = sqrt(t);
+  scalars[kFinite] = __builtin_isfinite(t) ? 1.0 : 0.0;
+}
+
+__global__ __launch_bounds__(kBlock) void k_norm_final(const NormFinalLaunch P) {
+  const int64_t J = norm_groups(P.n_chunks);
+  if (J == 0) {  // nothing owned: the norm of no elements
+    if (threadIdx.x == 0) write_norm(0.0, P.scalars);
+    return;
   }
-  for (; i < n; i += kFinalBlock) s += partials[i];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
-  __shared__ double part[kFinalBlock / 64];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-  __syncthreads();
+  const int64_t q = int64_t(blockIdx.x) * kNormGroup + threadIdx.x;
+  const double sj = block_sum(q < P.n_chunks ? P.partials[q] : 0.0);
+  __shared__ int last;
   if (threadIdx.x == 0) {
-    double t = part[0];
-    for (int w = 1; w < kFinalBlock / 64; ++w) t += part[w];
-    scalars[kNormSq] = t;
-    scalars[kNorm] = sqrt(t);
-    scalars[kFinite] = __builtin_isfinite(t) ? 1.0 : 0.0;
+    P.group_sums[blockIdx.x] = sj;
+    __threadfence();  // the group sum is visible before the count says so
+    last = atomicAdd(P.counter, 1u) == uint32_t(J - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();    // and every other group's sum is visible here
+  double s = 0.0;
+  for (int64_t j = threadIdx.x; j < J; j += kBlock) s += P.group_sums[j];
+  const double t = block_sum(s);
+  if (threadIdx.x == 0) {
+    write_norm(t, P.scalars);
+    *P.counter = 0u;
   }
 }
 
@@ -806,8 +848,11 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
 // Chunks are visited last to first: the step's last accumulate pass has just
 // written the accumulator front to back, so its final stretch is still in
 // the MI355X's memory-side Infinity Cache when this pass starts.
+#ifndef GRO_ADAMW_FORWARD
+#define GRO_ADAMW_FORWARD 0
+#endif
 __global__ __launch_bounds__(kBlock, GRO_ADAMW_MIN_BLOCKS) void k_adamw(const AdamWLaunch P) {
-  const int64_t q = P.n_chunks - 1 - int64_t(blockIdx.x);
+  const int64_t q = GRO_ADAMW_FORWARD ? int64_t(blockIdx.x) : P.n_chunks - 1 - int64_t(blockIdx.x);
   if (q >= P.n_chunks) return;
   if (P.scalars[kFinite] == 0.0) return;  // non-finite norm: skip the step
   AdamScalars k;
@@ -929,7 +974,8 @@ hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s) {
 
 hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
-  const int64_t blocks = (a.q_end - a.q_begin) + (a.q_begin & 7);
+  const int64_t blocks = GRO_WIN_MAP == 0 ? (a.q_end - a.q_begin) + (a.q_begin & 7)
+                                          : ((a.q_end - a.q_begin + 7) >> 3) * 8;
   hipLaunchKernelGGL(k_accumulate_window, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
@@ -941,9 +987,9 @@ hipError_t launch_norm_partials(const NormLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_norm_final(const double* partials, int64_t n_chunks, double* scalars,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(k_norm_final, dim3(1), dim3(kFinalBlock), 0, s, partials, n_chunks, scalars);
+hipError_t launch_norm_final(const NormFinalLaunch& a, hipStream_t s) {
+  const int64_t groups = norm_groups(a.n_chunks);
+  hipLaunchKernelGGL(k_norm_final, dim3(unsigned(groups > 0 ? groups : 1)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -235,6 +235,12 @@ extern "C" int gro_plan_create(const gro_tensor_desc* tensors, int32_t n_tensors
   off = uint64_t(align_up(int64_t(off + p->chunks.size() * sizeof(double)), 256));
   ws.tensor_off = off;
   off = uint64_t(align_up(int64_t(off + p->tensors.size() * sizeof(TensorDev)), 256));
+  const int64_t groups = norm_groups(int64_t(p->chunks.size()));
+  ws.group_off = off;
+  off = uint64_t(align_up(int64_t(off + uint64_t(groups) * sizeof(double)), 256));
+  ws.counter_off = off;
+  ws.counter_bytes = uint64_t(align_up(int64_t((groups + 1) * sizeof(uint32_t)), 256));
+  off += ws.counter_bytes;
   ws.total = off;
 
   p->count.assign(p->buckets.size(), 0);

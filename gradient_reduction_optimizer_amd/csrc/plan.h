@@ -54,8 +54,17 @@ static_assert(sizeof(BucketDev) == 32, "bucket table entry is 32 bytes");
 // Device scalars written by the norm's second stage.
 enum ScalarSlot { kNormSq = 0, kNorm = 1, kFinite = 2, kNumScalars = 8 };
 
+// The norm's second stage sums the chunk partials in two fixed-order levels:
+// groups of kNormGroup consecutive partials, then the group sums.
+constexpr int64_t kNormGroup = 256;
+constexpr int64_t norm_groups(int64_t n_chunks) { return (n_chunks + kNormGroup - 1) / kNormGroup; }
+
 struct WorkspaceLayout {
-  uint64_t bucket_off = 0, chunk_off = 0, partial_off = 0, scalar_off = 0, tensor_off = 0, total = 0;
+  uint64_t bucket_off = 0, chunk_off = 0, partial_off = 0, scalar_off = 0, tensor_off = 0;
+  uint64_t group_off = 0;    // FP64 group sums, one per kNormGroup chunks
+  uint64_t counter_off = 0;  // uint32 completion counters (zero between launches)
+  uint64_t counter_bytes = 0;
+  uint64_t total = 0;
 };
 
 inline int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
