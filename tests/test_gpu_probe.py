@@ -29,24 +29,27 @@ def _rand(n, seed, dtype=torch.float32):
     return torch.randn(n, generator=g, device="cuda").to(dtype)
 
 
-def test_probe_patterns_compute_what_they_read(lib):
+@pytest.mark.parametrize("wide", [False, True])
+def test_probe_patterns_compute_what_they_read(lib, wide):
+    """Patterns 0-2 (4 elements per lane access) and 3-5 (8 per lane)."""
+    off = 3 if wide else 0
     n = 3 * 4096
     s = torch.cuda.current_stream().cuda_stream
     gs = [_rand(n, 10 + j, torch.bfloat16) for j in range(3)]
     gp = (V * 3)(*[x.data_ptr() for x in gs])
     out = torch.zeros(n, device="cuda")
-    assert lib.gro_probe_stream(1, n, None, out.data_ptr(), None, None, None, gp, 3, s) == 0
+    assert lib.gro_probe_stream(1 + off, n, None, out.data_ptr(), None, None, None, gp, 3, s) == 0
     torch.cuda.synchronize()
     want = (gs[0].float() + gs[1].float()) + gs[2].float()
     assert torch.equal(out, want)
     old = out.clone()
-    assert lib.gro_probe_stream(2, n, None, out.data_ptr(), None, None, None, gp, 1, s) == 0
+    assert lib.gro_probe_stream(2 + off, n, None, out.data_ptr(), None, None, None, gp, 1, s) == 0
     torch.cuda.synchronize()
     assert torch.equal(out, old + gs[0].float())
     a, p, m, v = (_rand(n, 20 + j) for j in range(4))
     pb = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
     p0, m0, v0 = p.clone(), m.clone(), v.clone()
-    assert lib.gro_probe_stream(0, n, a.data_ptr(), p.data_ptr(), m.data_ptr(), v.data_ptr(), pb.data_ptr(),
+    assert lib.gro_probe_stream(0 + off, n, a.data_ptr(), p.data_ptr(), m.data_ptr(), v.data_ptr(), pb.data_ptr(),
                                 None, 0, s) == 0
     torch.cuda.synchronize()
     assert torch.equal(p, p0 - a) and torch.equal(m, m0 + a) and torch.equal(v, v0 + a * a)
@@ -62,4 +65,5 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.gro_probe_stream(1, 8192, None, out.data_ptr(), None, None, None, gp, 9, s) == -1  # k not built
     assert lib.gro_probe_stream(1, 8192, None, out.data_ptr(), None, None, None, gp, 17, s) == -1
     assert lib.gro_probe_stream(0, 8192, None, out.data_ptr(), None, None, None, None, 0, s) == -1  # missing arrays
+    assert lib.gro_probe_stream(4, 8192, None, out.data_ptr(), None, None, None, gp, 9, s) == -1  # k not built
     assert lib.gro_probe_stream(7, 8192, None, out.data_ptr(), None, None, None, gp, 1, s) == -1  # no such pattern
