@@ -11,6 +11,17 @@ dispatch of every counter in a counter_collection.csv.
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per
 launch for each kernel, scaled by the ratio of known to counted bytes of the
 plain copy kernel that ran in the same process (the calibration).
+
+    python -m gradient_reduction_optimizer_amd.profiling requests <copy bytes> <counter csv>... > requests.json
+
+`requests` counts bytes a second way, from the L2-to-fabric request counters
+binned by size (TCC_EA0_RDREQ_32B/_64B/_128B for reads, TCC_EA0_WRREQ and
+TCC_EA0_WRREQ_64B for writes): bytes = the sum of requests times their
+size, with no calibration.  The copy kernel's counted bytes against its
+known bytes check that count.  It also evaluates the gfx950 FETCH_SIZE
+formula on the same run (TCC_BUBBLE counted as the 128-byte reads, every
+other non-32-byte read as 64 bytes) to show where FETCH_SIZE's factor of
+two comes from.  Counters may come from several passes (CSV files).
 """
 from __future__ import annotations
 
@@ -77,6 +88,59 @@ def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
     return res
 
 
+def _per_dispatch_sums(paths):
+    """{kernel: {counter: [value per dispatch]}}, values of one dispatch
+    summed over the rows that report it (one row per counter instance or
+    one per dispatch, as rocprofv3 writes them)."""
+    acc = defaultdict(float)
+    kname = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            key = (path, r["Dispatch_Id"], r["Counter_Name"])
+            acc[key] += float(r["Counter_Value"])
+            kname[key] = short_name(r["Kernel_Name"])
+    out = defaultdict(lambda: defaultdict(list))
+    for key, val in acc.items():
+        out[kname[key]][key[2]].append(val)
+    return out
+
+
+def requests(copy_bytes: int, paths) -> dict:
+    v = _per_dispatch_sums(paths)
+
+    def avg(k, c, top=None):
+        xs = v.get(k, {}).get(c, [])
+        if top:
+            xs = sorted(xs)[-top:]
+        return sum(xs) / len(xs) if xs else None
+
+    res = {"kernel_source_sha256_16": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16],
+           "kernels": {}}
+    for k in OURS + ("copy",):
+        top = 3 if k == "copy" else None   # the calibration copies are the largest copy dispatches
+        c = {name: avg(k, name, top) for name in ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B",
+                                                   "TCC_EA0_RDREQ_128B", "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B",
+                                                   "TCC_BUBBLE", "TCC_EA0_RDREQ_DRAM", "TCC_EA0_WRREQ_DRAM")}
+        if c["TCC_EA0_RDREQ_128B"] is None or c["TCC_EA0_WRREQ"] is None:
+            continue
+        rd = 32 * c["TCC_EA0_RDREQ_32B"] + 64 * c["TCC_EA0_RDREQ_64B"] + 128 * c["TCC_EA0_RDREQ_128B"]
+        wr = 32 * (c["TCC_EA0_WRREQ"] - c["TCC_EA0_WRREQ_64B"]) + 64 * c["TCC_EA0_WRREQ_64B"]
+        e = {"dispatches": len(v[k]["TCC_EA0_RDREQ_128B"]), "requests_per_launch": c,
+             "read_bytes_per_launch": rd, "write_bytes_per_launch": wr, "bytes_per_launch": rd + wr,
+             "read_requests_binned_over_all": (c["TCC_EA0_RDREQ_32B"] + c["TCC_EA0_RDREQ_64B"] +
+                                               c["TCC_EA0_RDREQ_128B"]) / c["TCC_EA0_RDREQ"]
+             if c["TCC_EA0_RDREQ"] else None}
+        if c["TCC_BUBBLE"] is not None:
+            e["fetch_size_formula_bytes"] = (128 * c["TCC_BUBBLE"] + 32 * c["TCC_EA0_RDREQ_32B"] +
+                                             64 * (c["TCC_EA0_RDREQ"] - c["TCC_BUBBLE"] - c["TCC_EA0_RDREQ_32B"]))
+        if k == "copy":
+            e["known_bytes_each_way"] = copy_bytes
+            e["read_counted_over_known"] = rd / copy_bytes
+            e["write_counted_over_known"] = wr / copy_bytes
+        res["kernels"][k] = e
+    return res
+
+
 def counters(path: str) -> str:
     vals = defaultdict(lambda: defaultdict(list))
     for r in csv.DictReader(open(path)):
@@ -98,5 +162,7 @@ if __name__ == "__main__":
         print(kernel_stats(sys.argv[2]))
     elif sys.argv[1] == "counters":
         print(counters(sys.argv[2]))
+    elif sys.argv[1] == "requests":
+        print(json.dumps(requests(int(sys.argv[2]), sys.argv[3:]), indent=1))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4])), indent=1))

@@ -83,3 +83,79 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_exact_sum_of_squares_matches_a_correctly_rounded_sum():
+    """bench.py's all-cores oracle timing adds the workers' norm partials
+    exactly; rounded once, that must equal math.fsum of the squares (the
+    oracle's own correctly rounded sum) bit for bit, here on values that
+    span the FP32 range: subnormals, huge values, zeros, mixed signs."""
+    import math
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    rng = np.random.default_rng(5)
+    cases = [rng.standard_normal(10_000).astype(np.float32) * 1e-2,
+             (rng.standard_normal(5_000) * np.exp2(rng.integers(-140, 60, 5_000))).astype(np.float32),
+             np.array([0.0, -0.0, 1.0, np.float32(2.0 ** -149), -3.5e18], np.float32),
+             np.zeros(7, np.float32), np.zeros(0, np.float32)]
+    for x in cases:
+        want = math.fsum(float(t) * float(t) for t in x.astype(np.float64))
+        got = bench.exact_total([bench.exact_sum_of_squares(x)])
+        assert got == want, (got, want)
+        # the same sum split into uneven parts
+        cuts = sorted(rng.integers(0, x.size + 1, 3)) if x.size else []
+        parts = [bench.exact_sum_of_squares(p) for p in np.split(x, cuts)]
+        assert bench.exact_total(parts) == want
+    assert bench.exact_sum_of_squares(np.array([1.0, np.inf], np.float32)) is None
+
+
+def test_all_cores_oracle_timing_reproduces_one_core_bits():
+    """The all-cores timing harness ends in the same bits as the oracle's own
+    optimizer_window on one core (it raises otherwise), on the tiny set."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from gradient_reduction_optimizer_amd import synth
+    r = bench.cpu_baseline(synth.tiny(literal=True), 1.0, lambda *a: None, runs=3, max_workers=3)
+    assert r["bit_identical_across_core_counts"] is True
+    assert r["cores"] == min(3, len(os.sched_getaffinity(0)))
+    assert r["one_core"]["cores"] == 1 and len(r["runs_s"]) == 3 and len(r["one_core"]["runs_s"]) == 3
+    assert bench._pieces([5, 0, 7, 1], 3) == [[(0, 0, 4)], [(0, 4, 5), (2, 0, 3)], [(2, 3, 7), (3, 0, 1)]]
+
+
+def test_request_counters_give_bytes_without_calibration(tmp_path):
+    """Reads: 32/64/128-byte requests times their size; writes: 32/64-byte;
+    the FETCH_SIZE formula reads 128-byte requests only through TCC_BUBBLE,
+    so with TCC_BUBBLE at zero it reports half of all-128-byte reads.
+    Rows of one dispatch from several counter instances are summed."""
+    import json as _json
+    copy = "void at::native::elementwise_copy_kernel(...)"
+    win = "gro::(anonymous namespace)::k_accumulate_window(gro::WindowLaunch)"
+    rd, wr = tmp_path / "rd.csv", tmp_path / "wr.csv"
+    mib = 1 << 20
+    rows_rd, rows_wr = [], []
+    for d in range(3):  # copy: 1 MiB each way as 128-byte reads and 64-byte writes, two instances each
+        for half in (0, 1):
+            rows_rd += [(d, copy, "TCC_EA0_RDREQ", mib // 256), (d, copy, "TCC_EA0_RDREQ_32B", 0),
+                        (d, copy, "TCC_EA0_RDREQ_64B", 0), (d, copy, "TCC_EA0_RDREQ_128B", mib // 256)]
+            rows_wr += [(d, copy, "TCC_EA0_WRREQ", mib // 128), (d, copy, "TCC_EA0_WRREQ_64B", mib // 128),
+                        (d, copy, "TCC_BUBBLE", 0)]
+    rows_rd += [(7, win, "TCC_EA0_RDREQ", 110), (7, win, "TCC_EA0_RDREQ_32B", 4),
+                (7, win, "TCC_EA0_RDREQ_64B", 6), (7, win, "TCC_EA0_RDREQ_128B", 100)]
+    rows_wr += [(7, win, "TCC_EA0_WRREQ", 50), (7, win, "TCC_EA0_WRREQ_64B", 40), (7, win, "TCC_BUBBLE", 0)]
+    for path, rows in ((rd, rows_rd), (wr, rows_wr)):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=COLS)
+            w.writeheader()
+            for i, (d, k, c, val) in enumerate(rows):
+                w.writerow({"Correlation_Id": i, "Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": c,
+                            "Counter_Value": val})
+    r = P.requests(mib, [str(rd), str(wr)])
+    c = r["kernels"]["copy"]
+    assert c["read_counted_over_known"] == pytest.approx(1.0) and c["write_counted_over_known"] == pytest.approx(1.0)
+    assert c["fetch_size_formula_bytes"] == pytest.approx(mib / 2)
+    k = r["kernels"]["k_accumulate_window"]
+    assert k["read_bytes_per_launch"] == 32 * 4 + 64 * 6 + 128 * 100
+    assert k["write_bytes_per_launch"] == 32 * 10 + 64 * 40
+    assert k["fetch_size_formula_bytes"] == 32 * 4 + 64 * 106
+    _json.dumps(r)
