@@ -32,9 +32,10 @@ GRO_GRAD_BF16, GRO_GRAD_FP32 = 0, 1
 GRO_OWNER_MEAN, GRO_OWNER_SUM, GRO_OWNER_LOCAL_SHARD, GRO_OWNER_LOCAL_REDUCED, GRO_OWNER_EXCLUDED = range(5)
 OWNER_NAMES = ("mean", "sum", "local_shard", "local_reduced", "excluded")
 GRO_MAX_NDIM = 8
+GRO_STATIC_WORKSPACE_BYTES = 16777216
 
 EXPORTS = ("gro_plan_create", "gro_plan_destroy", "gro_plan_get_info", "gro_plan_tensor",
-           "gro_plan_bucket", "gro_plan_bind", "gro_accumulate", "gro_accumulate_window",
+           "gro_plan_bucket", "gro_plan_bind", "gro_plan_bind_static", "gro_accumulate", "gro_accumulate_window",
            "gro_accumulate_microbatches",
            "gro_reduce_norm", "gro_plan_get_norm", "gro_clip_adamw", "gro_init_uniform",
            "gro_last_error")
@@ -104,6 +105,7 @@ def load() -> ctypes.CDLL:
     L.gro_plan_tensor.argtypes = [P, I32, ctypes.POINTER(gro_tensor_layout)]
     L.gro_plan_bucket.argtypes = [P, I32, ctypes.POINTER(gro_bucket_info)]
     L.gro_plan_bind.argtypes = [P, P, U64, P]
+    L.gro_plan_bind_static.argtypes = [P, P]
     L.gro_accumulate.argtypes = [P, I32, I32, ctypes.POINTER(P), P, I32, I32, P]
     L.gro_accumulate_window.argtypes = [P, I32, I32, ctypes.POINTER(P), I32, P, P]
     L.gro_accumulate_microbatches.argtypes = [P, I32, I32, ctypes.POINTER(P), I32, I32, I32, P, P]
@@ -190,6 +192,11 @@ def gro_plan_bucket(plan: int, b: int) -> dict:
 def gro_plan_bind(plan: int, d_workspace: int, nbytes: int, stream: int = 0) -> None:
     _check(load().gro_plan_bind(ctypes.c_void_p(plan), ctypes.c_void_p(d_workspace), int(nbytes),
                                 ctypes.c_void_p(stream)))
+
+
+def gro_plan_bind_static(plan: int, stream: int = 0) -> None:
+    """Bind to the library's own per-GPU workspace (no allocation)."""
+    _check(load().gro_plan_bind_static(ctypes.c_void_p(plan), ctypes.c_void_p(stream)))
 
 
 def _pointer_array(ptrs: Sequence[int], expected: int, what: str):

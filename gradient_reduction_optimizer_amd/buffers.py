@@ -52,9 +52,12 @@ class Plan:
 
 class DeviceState:
     """FP32 accumulator / master / m / v, the BF16 parameter copy and the
-    workspace for one plan, allocated with torch on ``device`` and bound."""
+    workspace for one plan, allocated with torch on ``device`` and bound.
+    With ``static_workspace`` no workspace is allocated: the plan is bound
+    to the library's own per-GPU workspace (gro_plan_bind_static)."""
 
-    def __init__(self, plan: Plan, device="cuda", with_bf16: bool = True, stream=None):
+    def __init__(self, plan: Plan, device="cuda", with_bf16: bool = True, stream=None,
+                 static_workspace: bool = False):
         import torch
         self.plan = plan
         self.device = torch.device(device)
@@ -66,6 +69,10 @@ class DeviceState:
         self.v = torch.zeros(n, **f32)
         self.p_bf16 = torch.zeros(n, dtype=torch.bfloat16, device=self.device) if with_bf16 else None
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if static_workspace:
+            self.workspace, self.ws_ptr, self.ws_bytes = None, None, 0
+            B.gro_plan_bind_static(plan.handle, self.stream.cuda_stream)
+            return
         nbytes = int(plan.info["workspace_bytes"])
         self.workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=self.device)
         base = self.workspace.data_ptr()

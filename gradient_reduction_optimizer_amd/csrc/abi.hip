@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -22,12 +23,48 @@
 
 using namespace gro;
 
+// The library-owned workspace of gro_plan_bind_static: one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side
+// shadow, not device memory; its device address comes from
+// hipGetSymbolAddress (once per device, below) and only that address is
+// ever handed to the runtime or to a kernel.
+static __device__ __align__(256) unsigned char scratch[GRO_STATIC_WORKSPACE_BYTES];
+
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int hip_fail(hipError_t e, const char* what) {
   return set_error(GRO_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Device address of `scratch` on each device, looked up the first time a
+// plan is bound to it on that device (with that device current).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+// Bumped by every gro_plan_bind_static on the device: a plan bound earlier
+// no longer owns the array once another plan has been bound to it.
+uint64_t g_scratch_gen[kMaxDevices] = {};
+
+bool scratch_still_owned(const gro_plan* p) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return p->device >= 0 && p->device < kMaxDevices && g_scratch_gen[p->device] == p->static_gen;
+}
+
+int scratch_address(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return set_error(GRO_E_INVALID, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr || (reinterpret_cast<uintptr_t>(ptr) & 255u))
+      return set_error(GRO_E_HIP, "static workspace has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return GRO_OK;
 }
 
 int check_bound(const gro_plan* p) {
@@ -38,6 +75,8 @@ int check_bound(const gro_plan* p) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != p->device)
     return set_error(GRO_E_STATE, "plan is bound on device %d, current device is %d", p->device, dev);
+  if (p->static_ws && !scratch_still_owned(p))
+    return set_error(GRO_E_STATE, "the static workspace has been bound to another plan since; bind again");
   return GRO_OK;
 }
 
@@ -78,10 +117,15 @@ namespace {
 
 // Upload the plan's tables into `ws` on `stream`, clear the norm's
 // completion counters (they must start at zero; every kernel that counts
-// returns them to zero), wait, and mark the plan bound there.
-int bind_to(gro_plan* p, char* ws, void* stream) {
+// returns them to zero), wait, and mark the plan bound there.  Shared by
+// gro_plan_bind and gro_plan_bind_static; for the static workspace the norm
+// scalars are cleared too (the array keeps what the plan bound before left
+// there) and the binding's generation is recorded.
+int bind_to(gro_plan* p, char* ws, void* stream, bool is_static) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipMemsetAsync(ws + p->ws.counter_off, 0, p->ws.counter_bytes, s);
+  if (e == hipSuccess && is_static)
+    e = hipMemsetAsync(ws + p->ws.scalar_off, 0, kNumScalars * sizeof(double), s);
   if (e == hipSuccess && !p->bucket_dev.empty())
     e = hipMemcpyAsync(ws + p->ws.bucket_off, p->bucket_dev.data(),
                        p->bucket_dev.size() * sizeof(BucketDev), hipMemcpyHostToDevice, s);
@@ -97,6 +141,11 @@ int bind_to(gro_plan* p, char* ws, void* stream) {
   p->bound = true;
   p->device = dev;
   p->norm_valid = false;
+  p->static_ws = is_static;
+  if (is_static) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p->static_gen = ++g_scratch_gen[dev];
+  }
   reset_window(p);
   return GRO_OK;
 }
@@ -111,7 +160,26 @@ extern "C" int gro_plan_bind(gro_plan* p, void* d_workspace, uint64_t bytes, voi
   if (bytes < p->ws.total)
     return set_error(GRO_E_INVALID, "workspace has %llu bytes, plan needs %llu",
                      (unsigned long long)bytes, (unsigned long long)p->ws.total);
-  return bind_to(p, static_cast<char*>(d_workspace), stream);
+  return bind_to(p, static_cast<char*>(d_workspace), stream, false);
+}
+
+extern "C" int gro_plan_bind_static(gro_plan* p, void* stream) {
+  clear_error();
+  if (p == nullptr) return set_error(GRO_E_INVALID, "NULL argument");
+  if (p->ws.total > uint64_t(GRO_STATIC_WORKSPACE_BYTES))
+    return set_error(GRO_E_INVALID, "plan needs %llu workspace bytes, the static workspace holds %llu",
+                     (unsigned long long)p->ws.total, (unsigned long long)GRO_STATIC_WORKSPACE_BYTES);
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  char* ws = nullptr;
+  const int rc = scratch_address(dev, &ws);
+  if (rc != GRO_OK) return rc;
+  // The array may still be in use by the plan bound to it before, on any
+  // stream: let all device work finish before overwriting its tables.
+  const hipError_t se = hipDeviceSynchronize();
+  if (se != hipSuccess) return hip_fail(se, "hipDeviceSynchronize");
+  return bind_to(p, ws, stream, true);
 }
 
 extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_grad_buckets,

@@ -91,6 +91,8 @@ struct gro_plan {
   char* d_ws = nullptr;
   bool bound = false;
   int device = -1;
+  bool static_ws = false;               // bound to the library's static workspace
+  uint64_t static_gen = 0;              // which binding of that workspace is this plan's
 
   // Window bookkeeping (host side, validated before any launch).
   std::vector<int32_t> count;          // microbatches accumulated per bucket

@@ -42,8 +42,8 @@
  *    a thread-local message (gro_last_error).  Validation precedes any device
  *    work.  Non-finite data is reported through gro_plan_get_norm's `finite`
  *    flag, not a return code, because device work is asynchronous.
- *  - Only gro_plan_bind, gro_init_uniform and gro_plan_get_norm wait for the
- *    device.
+ *  - Only gro_plan_bind, gro_plan_bind_static, gro_init_uniform and
+ *    gro_plan_get_norm wait for the device.
  *  - Not thread-safe per plan; distinct plans may be used from distinct
  *    threads.
  */
@@ -191,6 +191,33 @@ int gro_plan_bucket(const gro_plan* plan, int32_t b, gro_bucket_info* out);
  * workspace (>= workspace_bytes, 256-byte aligned) on `stream`, and wait for
  * the copy.  Must precede the calls below; may be repeated (rebinding). */
 int gro_plan_bind(gro_plan* plan, void* d_workspace, uint64_t bytes, void* stream);
+
+/* Bytes of the library's own device workspace, one per GPU, used by
+ * gro_plan_bind_static (enough for about 700,000 chunks, i.e. plans of up to
+ * about 2.8e9 elements). */
+#define GRO_STATIC_WORKSPACE_BYTES 16777216ull
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): gro_plan_bind on a
+ * workspace the library holds itself -- a static device array of
+ * GRO_STATIC_WORKSPACE_BYTES per GPU, kept until the process ends -- instead
+ * of one the caller allocates.  Every later call of the plan behaves as
+ * after gro_plan_bind; the caller still passes the accumulator, the states
+ * and the gradient buffers.  Allocates nothing, frees nothing.
+ *  - A plan whose workspace_bytes exceeds GRO_STATIC_WORKSPACE_BYTES:
+ *    GRO_E_INVALID, nothing done.
+ *  - All plans bound this way on one GPU share that GPU's array.  Binding
+ *    waits for all work on the current device to finish, then overwrites
+ *    the array; from then on a plan bound to it earlier is rejected with
+ *    GRO_E_STATE until it is bound again.  Device calls of two plans that
+ *    overlap on one GPU would race on the array, which is why only the
+ *    last plan bound may use it.
+ *  - Binding clears what must start at zero -- the norm's completion
+ *    counters (every bind does) -- and the norm scalars; every other byte
+ *    of the array is written by a kernel before one reads it.
+ *  - Waits for its own upload, like gro_plan_bind.  Not for use inside a
+ *    graph capture (it synchronizes); bind first, then capture. */
+int gro_plan_bind_static(gro_plan* plan, void* stream);
 
 /* Reduce + cast + accumulate one microbatch for buckets [b0, b1) -- NeMo
  * Automodel issue #3857, section "Why this needs separate work" (Replicate
