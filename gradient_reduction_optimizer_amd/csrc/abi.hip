@@ -108,20 +108,7 @@ void reset_window(gro_plan* p) {
   std::fill(p->partials_ready.begin(), p->partials_ready.end(), 0);
   p->acc_ptr = nullptr;
   p->norm_done = false;
-  p->finish_done = false;
   p->norm_window = 0;
-}
-
-// The norm's second stage at the end of a stage-1 launch, when the build
-// fuses it and the launch writes every chunk partial of the plan.
-NormFinish norm_finish(const gro_plan* p, bool all_partials) {
-  NormFinish f;
-  f.active = (all_partials && fused_norm_finish()) ? 1 : 0;
-  f.n_chunks = int64_t(p->chunks.size());
-  f.group_sums = dev_groups(p);
-  f.counters = dev_counters(p);
-  f.scalars = dev_scalars(p);
-  return f;
 }
 
 }  // namespace
@@ -225,8 +212,6 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
   if (rc != GRO_OK) return rc;
 
   const bool fuse = window_size > 0 && micro_index == window_size - 1;
-  // One launch that writes every partial of the plan also finishes the norm.
-  const bool finish = fuse && b0 == 0 && b1 == nb && nb <= kMaxBucketsPerLaunch;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t lb = b0; lb < b1; lb += kMaxBucketsPerLaunch) {
     const int32_t le = (b1 - lb) < kMaxBucketsPerLaunch ? b1 : lb + kMaxBucketsPerLaunch;
@@ -245,7 +230,6 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
     a.micro_index = micro_index;
     a.fuse_norm = fuse ? 1 : 0;
     a.window = window_size;
-    a.finish = norm_finish(p, finish);
     const hipError_t e = launch_accumulate(a, s);
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   }
@@ -255,7 +239,6 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
   }
   p->acc_ptr = d_acc;
   p->norm_done = false;
-  p->finish_done = finish && fused_norm_finish();
   return GRO_OK;
 }
 
@@ -306,8 +289,6 @@ int accumulate_group(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_g
   const bool fuse = window_size > 0 && first_micro + n == window_size;
   // Buckets of one launch: n * buckets <= kMaxBucketsPerLaunch pointers.
   const int32_t per = kMaxBucketsPerLaunch / n;
-  // One launch that writes every partial of the plan also finishes the norm.
-  const bool finish = fuse && b0 == 0 && b1 == nb && nb <= per;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t lb = b0; lb < b1; lb += per) {
     const int32_t le = (b1 - lb) < per ? b1 : lb + per;
@@ -329,7 +310,6 @@ int accumulate_group(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_g
         a.grads[k * (le - lb) + (b - lb)] = d_grad_buckets[int64_t(k) * span + (b - b0)];
     a.acc = d_acc;
     a.partials = dev_partials(p);
-    a.finish = norm_finish(p, finish);
     const hipError_t e = launch_accumulate_window(a, s);
     if (e != hipSuccess) return hip_fail(e, "accumulate-window launch");
   }
@@ -339,7 +319,6 @@ int accumulate_group(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_g
   }
   p->acc_ptr = d_acc;
   p->norm_done = false;
-  p->finish_done = finish && fused_norm_finish();
   return GRO_OK;
 }
 
@@ -374,14 +353,6 @@ extern "C" int gro_reduce_norm(gro_plan* p, const float* d_acc, int32_t window_s
     return set_error(GRO_E_STATE, "d_acc is not the accumulator of this window");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p->finish_done) {
-    // the window's last accumulate pass wrote every partial and the norm
-    p->norm_done = true;
-    p->norm_valid = true;
-    p->norm_window = window_size;
-    p->norm_stream = stream;
-    return GRO_OK;
-  }
   // Stage 1 for runs of buckets whose partials the last accumulate did not write.
   int32_t b = 0;
   while (b < nb) {

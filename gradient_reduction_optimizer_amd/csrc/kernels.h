@@ -12,19 +12,6 @@ namespace gro {
 // Buckets whose gradient pointers travel in one launch's kernel arguments.
 constexpr int kMaxBucketsPerLaunch = 64;
 
-// The norm's second stage run at the end of a stage-1 pass that writes every
-// chunk partial of the plan (active = 1): the last workgroup of each group
-// of kNormGroup chunks adds the group's partials, the last of those adds the
-// group sums.  counters[0] counts finished groups, counters[1 + j] the
-// finished chunks of group j; all are zero before and after.
-struct NormFinish {
-  int32_t active;
-  int64_t n_chunks;
-  double* group_sums;
-  uint32_t* counters;
-  double* scalars;
-};
-
 struct AccumulateLaunch {
   const ChunkDev* chunks;   // device chunk table
   const BucketDev* buckets; // device bucket table
@@ -38,7 +25,6 @@ struct AccumulateLaunch {
   int32_t micro_index;
   int32_t fuse_norm;
   int32_t window;           // microbatches in the window (used when fuse_norm)
-  NormFinish finish;        // the norm's second stage, when this launch writes every partial
 };
 
 // A whole accumulation window in one pass: grads[k * n_buckets + j] is
@@ -57,7 +43,6 @@ struct WindowLaunch {
   const void* grads[kMaxBucketsPerLaunch];
   float* acc;
   double* partials;
-  NormFinish finish;
 };
 
 struct NormLaunch {
@@ -74,12 +59,9 @@ struct NormFinalLaunch {
   const double* partials;
   int64_t n_chunks;
   double* group_sums;       // one per kNormGroup chunks
-  uint32_t* counter;        // counters[0] of NormFinish
+  uint32_t* counter;
   double* scalars;
 };
-
-// Whether the stage-1 passes finish the norm themselves (see NormFinish).
-bool fused_norm_finish();
 
 struct AdamWLaunch {
   const ChunkDev* chunks;

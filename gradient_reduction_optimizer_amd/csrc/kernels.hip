@@ -168,73 +168,6 @@ __device__ double block_sum(double x) {
   return t;
 }
 
-// ------------------------------------------------ norm, stage 2 pieces
-// Two fixed-order levels, so the result never depends on launch shape or on
-// which workgroup runs when:
-//   group sum j = the kNormGroup partials kNormGroup*j .. (one per lane, lane
-//                 t takes partial kNormGroup*j + t; butterfly, then the wave
-//                 totals in wave order);
-//   total       = the group sums (lane t adds sums t, t + kBlock, ... in that
-//                 order; butterfly; wave totals in order).
-static_assert(kNormGroup == kBlock, "one partial per lane in a group sum");
-
-__device__ __forceinline__ double group_sum(const double* partials, int64_t n_chunks, int64_t j) {
-  const int64_t q = j * kNormGroup + threadIdx.x;
-  return block_sum(q < n_chunks ? partials[q] : 0.0);
-}
-
-__device__ __forceinline__ double total_of_groups(const double* group_sums, int64_t groups) {
-  double s = 0.0;
-  for (int64_t j = threadIdx.x; j < groups; j += kBlock) s += group_sums[j];
-  return block_sum(s);
-}
-
-__device__ __forceinline__ void write_norm(double t, double* scalars) {
-  scalars[kNormSq] = t;
-  scalars[kNorm] = sqrt(t);
-  scalars[kFinite] = __builtin_isfinite(t) ? 1.0 : 0.0;
-}
-
-#ifndef GRO_FUSED_FINAL
-#define GRO_FUSED_FINAL 0
-#endif
-
-// Called by every workgroup of a stage-1 pass that writes all partials,
-// after its thread 0 wrote partial q: completion counters find the last
-// workgroup of q's group (which adds the group) and the last group (whose
-// workgroup adds the group sums and writes the norm).  The counters only
-// say who is last; no atomic operation touches a sum.
-__device__ void finish_norm(const NormFinish& F, const double* partials, int64_t q) {
-  __shared__ int last_in_group, last_group;
-  const int64_t j = q / kNormGroup;
-  const int64_t groups = norm_groups(F.n_chunks);
-  const int64_t left = F.n_chunks - j * kNormGroup;
-  const uint32_t in_group = uint32_t(left < kNormGroup ? left : kNormGroup);
-  __syncthreads();  // block_sum's LDS is free again; the partial is written
-  if (threadIdx.x == 0) {
-    __threadfence();  // partial q is visible before the count says so
-    last_in_group = atomicAdd(F.counters + 1 + j, 1u) == in_group - 1;
-  }
-  __syncthreads();
-  if (!last_in_group) return;
-  __threadfence();    // every partial of the group is visible here
-  const double sj = group_sum(partials, F.n_chunks, j);
-  if (threadIdx.x == 0) {
-    F.group_sums[j] = sj;
-    F.counters[1 + j] = 0u;
-    __threadfence();
-    last_group = atomicAdd(F.counters, 1u) == uint32_t(groups - 1);
-  }
-  __syncthreads();
-  if (!last_group) return;
-  __threadfence();
-  const double t = total_of_groups(F.group_sums, groups);
-  if (threadIdx.x == 0) {
-    write_norm(t, F.scalars);
-    F.counters[0] = 0u;
-  }
-}
-
 // Chunk index of this workgroup, placed so that q == blockIdx.x (mod 8).
 __device__ __forceinline__ int64_t chunk_of_block(int64_t q_begin) {
   return q_begin - (q_begin & 7) + int64_t(blockIdx.x);
@@ -456,7 +389,6 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
   if (c.fuse) {
     const double t = block_sum(ss);
     if (threadIdx.x == 0) P.partials[q] = t;
-    if (GRO_FUSED_FINAL && P.finish.active) finish_norm(P.finish, P.partials, q);
   }
 }
 
@@ -687,7 +619,6 @@ __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch
   if (c.fuse) {
     const double t = block_sum(ss);
     if (threadIdx.x == 0) P.partials[q] = t;
-    if (GRO_FUSED_FINAL && P.finish.active) finish_norm(P.finish, P.partials, q);
   }
 }
 
@@ -759,16 +690,33 @@ __global__ __launch_bounds__(kBlock) void k_norm_partials(const NormLaunch P) {
 }
 
 // ------------------------------------------------------- norm, stage 2
-// One workgroup per group of kNormGroup partials adds its group; the
-// workgroup that finishes last -- found with a completion counter, which it
-// returns to zero -- adds the group sums and writes the norm.
+// Two fixed-order levels, so the result never depends on launch shape or on
+// which workgroup runs when:
+//   group sum j = the kNormGroup partials kNormGroup*j .. (one per lane, lane
+//                 t takes partial kNormGroup*j + t; butterfly, then the wave
+//                 totals in wave order);
+//   total       = the group sums (lane t adds sums t, t + kBlock, ... in that
+//                 order; butterfly; wave totals in order).
+// One workgroup per group.  The workgroup that finishes last -- found with a
+// completion counter, which it returns to zero -- adds the group sums and
+// writes the norm.  The counter only says who is last; no atomic operation
+// touches a sum.
+static_assert(kNormGroup == kBlock, "one partial per lane in a group sum");
+
+__device__ __forceinline__ void write_norm(double t, double* scalars) {
+  scalars[kNormSq] = t;
+  scalars[kNorm] = sqrt(t);
+  scalars[kFinite] = __builtin_isfinite(t) ? 1.0 : 0.0;
+}
+
 __global__ __launch_bounds__(kBlock) void k_norm_final(const NormFinalLaunch P) {
   const int64_t J = norm_groups(P.n_chunks);
   if (J == 0) {  // nothing owned: the norm of no elements
     if (threadIdx.x == 0) write_norm(0.0, P.scalars);
     return;
   }
-  const double sj = group_sum(P.partials, P.n_chunks, blockIdx.x);
+  const int64_t q = int64_t(blockIdx.x) * kNormGroup + threadIdx.x;
+  const double sj = block_sum(q < P.n_chunks ? P.partials[q] : 0.0);
   __shared__ int last;
   if (threadIdx.x == 0) {
     P.group_sums[blockIdx.x] = sj;
@@ -778,7 +726,9 @@ __global__ __launch_bounds__(kBlock) void k_norm_final(const NormFinalLaunch P) 
   __syncthreads();
   if (!last) return;
   __threadfence();    // and every other group's sum is visible here
-  const double t = total_of_groups(P.group_sums, J);
+  double s = 0.0;
+  for (int64_t j = threadIdx.x; j < J; j += kBlock) s += P.group_sums[j];
+  const double t = block_sum(s);
   if (threadIdx.x == 0) {
     write_norm(t, P.scalars);
     *P.counter = 0u;
@@ -1007,8 +957,6 @@ __global__ __launch_bounds__(kBlock) void k_init_uniform(const InitLaunch P) {
 }
 
 }  // namespace
-
-bool fused_norm_finish() { return GRO_FUSED_FINAL != 0; }
 
 // ------------------------------------------------------------ launchers
 hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s) {

@@ -99,7 +99,6 @@ struct gro_plan {
   std::vector<uint8_t> partials_ready; // norm partials written by the last accumulate
   const float* acc_ptr = nullptr;      // accumulator used in this window
   bool norm_done = false;               // a norm of the current window is on the device
-  bool finish_done = false;             // the last stage-1 pass also finished the norm
   bool norm_valid = false;              // some norm has been computed since binding
   int32_t norm_window = 0;
   void* norm_stream = nullptr;
