@@ -452,10 +452,10 @@ class StepTimer:
         self.c_mix = sum(bk["len"] * bk["slots"] for bk in self.plan.buckets)  # sum over elements of c
         self.step_no = 0
         self.flush_buf = flush_buf
-        # Per-call events on every step would add ~4 us per event to the
-        # steps they measure (~5 % of a draft-67m step), so inside the timed
-        # region they are recorded on every `sample_every`-th step only.
-        self.sample_every = max(1, args.steps // 10)
+        # An event pair around every call adds ~4 us per event to the steps
+        # it measures (~5 % of a draft-67m step), so the timed steps carry no
+        # events; per-call durations come from this many further steps.
+        self.event_steps = max(5, min(args.steps, 20))
 
     def flush(self):
         # An untimed read of an unrelated buffer much larger than the 256 MB
@@ -512,10 +512,10 @@ class StepTimer:
         return "k_accumulate_window", 1, n * 2 * c + 4 * N   # all n microbatches, one accumulator write
 
     def time_mode(self, mode: str, n: int, groups=None) -> dict:
-        """Warm up, then time exactly `steps` steps (wall clock between two
-        device synchronisations); HIP events recorded on the launch stream
-        around every call of every sample_every-th step give the per-kernel
-        durations and the per-step spread."""
+        """Warm up, then time exactly `steps` steps, with no events, by the
+        wall clock between two device synchronisations.  Then event_steps
+        further steps with a HIP event pair on the launch stream around every
+        call give the per-kernel durations and the per-step spread."""
         torch, args = self.torch, self.args
         ev = {"k_accumulate": [], "k_accumulate_window": [], "k_accumulate_group": [], "k_norm_final": [],
               "k_adamw": []}
@@ -523,10 +523,13 @@ class StepTimer:
             self.one_step(mode, n, None, groups)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            self.one_step(mode, n, ev if i % self.sample_every == 0 else None, groups)
+        for _ in range(args.steps):
+            self.one_step(mode, n, None, groups)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        for _ in range(self.event_steps):
+            self.one_step(mode, n, ev, groups)
+        torch.cuda.synchronize()
         acc_name, acc_launches, acc_launch = self.alg_bytes(mode, n, groups)
         # Per-step spread: each sampled step from its first call's start
         # event to its AdamW end event.
@@ -666,9 +669,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": wnd["ms_per_step"],
         "step_ms_events": wnd["step_ms_events"],
-        "event_sampling": f"per-call HIP events on every {t.sample_every}th timed step "
-                          f"({len(range(0, args.steps, t.sample_every))} of {args.steps}); ms_per_step is the wall "
-                          "clock of all timed steps",
+        "event_sampling": f"ms_per_step is the wall clock of the {args.steps} timed steps, which carry no events; "
+                          f"per-call HIP event durations and step_ms_events come from {t.event_steps} further steps "
+                          "with an event pair around every call",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
