@@ -40,9 +40,18 @@ def short_name(name: str) -> str:
     for k in OURS:  # longest names first
         if k + "(" in name or name.endswith(k) or f"::{k}" in name:
             return k
+    if "probe_" in name:  # stream probes: kernel and template arguments, e.g. probe_window<16, 4>
+        i = name.index("probe_")
+        j = name.find(">", i)
+        return name[i:j + 1] if j > 0 else name[i:].split("(")[0]
     if "copyBuffer" in name or "copy" in name.lower():
         return "copy"
     return name[:60]
+
+
+def _ours_and_probes(names):
+    """This library's kernels in OURS order, then the probe kernels sorted."""
+    return [k for k in OURS if k in names] + sorted(k for k in names if k.startswith("probe_"))
 
 
 def kernel_stats(path: str) -> str:
@@ -79,7 +88,7 @@ def traffic(fetch_csv: str, write_csv: str, copy_bytes: int) -> dict:
                            "fetch_scale": scale_f, "write_scale": scale_w},
            "kernel_source_sha256_16": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16],
            "kernels": {}}
-    for k in OURS:
+    for k in _ours_and_probes(f.keys()):
         if k in f and k in w:
             fb = sum(f[k]) / len(f[k]) * 1024 * scale_f
             wb = sum(w[k]) / len(w[k]) * 1024 * scale_w
@@ -116,7 +125,7 @@ def requests(copy_bytes: int, paths) -> dict:
 
     res = {"kernel_source_sha256_16": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16],
            "kernels": {}}
-    for k in OURS + ("copy",):
+    for k in _ours_and_probes(v.keys()) + ["copy"]:
         top = 3 if k == "copy" else None   # the calibration copies are the largest copy dispatches
         c = {name: avg(k, name, top) for name in ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B",
                                                    "TCC_EA0_RDREQ_128B", "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B",
@@ -145,11 +154,11 @@ def counters(path: str) -> str:
     vals = defaultdict(lambda: defaultdict(list))
     for r in csv.DictReader(open(path)):
         k = short_name(r["Kernel_Name"])
-        if k in OURS:
+        if k in OURS or k.startswith("probe_"):
             vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
     names = sorted({c for k in vals for c in vals[k]})
     out = ["kernel | dispatches | " + " | ".join(names)]
-    for k in OURS:
+    for k in _ours_and_probes(vals.keys()):
         if k in vals:
             n = max(len(v) for v in vals[k].values())
             out.append(f"{k} | {n} | " + " | ".join(

@@ -159,3 +159,10 @@ def test_request_counters_give_bytes_without_calibration(tmp_path):
     assert k["write_bytes_per_launch"] == 32 * 10 + 64 * 40
     assert k["fetch_size_formula_bytes"] == 32 * 4 + 64 * 106
     _json.dumps(r)
+
+
+def test_probe_kernels_keep_their_template_arguments():
+    assert P.short_name("void (anonymous namespace)::probe_window<16, 8>((anonymous namespace)::Streams)") == \
+        "probe_window<16, 8>"
+    assert P.short_name("void (anonymous namespace)::probe_adamw<4>((anonymous namespace)::Streams, long)") == \
+        "probe_adamw<4>"
