@@ -692,16 +692,17 @@ __global__ __launch_bounds__(kBlock) void k_norm_partials(const NormLaunch P) {
 // ------------------------------------------------------- norm, stage 2
 // Two fixed-order levels, so the result never depends on launch shape or on
 // which workgroup runs when:
-//   group sum j = the kNormGroup partials kNormGroup*j .. (one per lane, lane
-//                 t takes partial kNormGroup*j + t; butterfly, then the wave
-//                 totals in wave order);
-//   total       = the group sums (lane t adds sums t, t + kBlock, ... in that
-//                 order; butterfly; wave totals in order).
+//   group sum j = the kNormGroup partials from kNormGroup*j on: lane t adds
+//                 partials kNormGroup*j + t + kBlock*i for i = 0, 1, ... in
+//                 that order, then a butterfly and the wave totals in order;
+//   total       = the group sums, lane t adding sums t, t + kBlock, ... in
+//                 order, then a butterfly and the wave totals in order.
 // One workgroup per group.  The workgroup that finishes last -- found with a
 // completion counter, which it returns to zero -- adds the group sums and
 // writes the norm.  The counter only says who is last; no atomic operation
 // touches a sum.
-static_assert(kNormGroup == kBlock, "one partial per lane in a group sum");
+constexpr int kGroupPerLane = int(kNormGroup / kBlock);
+static_assert(kNormGroup % kBlock == 0, "whole lanes per group");
 
 __device__ __forceinline__ void write_norm(double t, double* scalars) {
   scalars[kNormSq] = t;
@@ -715,8 +716,17 @@ __global__ __launch_bounds__(kBlock) void k_norm_final(const NormFinalLaunch P) 
     if (threadIdx.x == 0) write_norm(0.0, P.scalars);
     return;
   }
-  const int64_t q = int64_t(blockIdx.x) * kNormGroup + threadIdx.x;
-  const double sj = block_sum(q < P.n_chunks ? P.partials[q] : 0.0);
+  const int64_t q0 = int64_t(blockIdx.x) * kNormGroup + threadIdx.x;
+  double x[kGroupPerLane];
+#pragma unroll
+  for (int i = 0; i < kGroupPerLane; ++i) {  // all loads issued before any add
+    const int64_t q = q0 + int64_t(i) * kBlock;
+    x[i] = q < P.n_chunks ? P.partials[q] : 0.0;
+  }
+  double s = x[0];
+#pragma unroll
+  for (int i = 1; i < kGroupPerLane; ++i) s += x[i];
+  const double sj = block_sum(s);
   __shared__ int last;
   if (threadIdx.x == 0) {
     P.group_sums[blockIdx.x] = sj;
@@ -726,11 +736,11 @@ __global__ __launch_bounds__(kBlock) void k_norm_final(const NormFinalLaunch P) 
   __syncthreads();
   if (!last) return;
   __threadfence();    // and every other group's sum is visible here
-  double s = 0.0;
-  for (int64_t j = threadIdx.x; j < J; j += kBlock) s += P.group_sums[j];
-  const double t = block_sum(s);
+  double t = 0.0;
+  for (int64_t j = threadIdx.x; j < J; j += kBlock) t += P.group_sums[j];
+  const double total = block_sum(t);
   if (threadIdx.x == 0) {
-    write_norm(t, P.scalars);
+    write_norm(total, P.scalars);
     *P.counter = 0u;
   }
 }

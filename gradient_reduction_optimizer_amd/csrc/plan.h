@@ -56,7 +56,7 @@ enum ScalarSlot { kNormSq = 0, kNorm = 1, kFinite = 2, kNumScalars = 8 };
 
 // The norm's second stage sums the chunk partials in two fixed-order levels:
 // groups of kNormGroup consecutive partials, then the group sums.
-constexpr int64_t kNormGroup = 256;
+constexpr int64_t kNormGroup = 2048;
 constexpr int64_t norm_groups(int64_t n_chunks) { return (n_chunks + kNormGroup - 1) / kNormGroup; }
 
 struct WorkspaceLayout {
