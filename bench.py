@@ -511,15 +511,16 @@ class StepTimer:
             return "k_accumulate_group", len(groups), (n * 2 * c + (4 + 8 * (len(groups) - 1)) * N) / len(groups)
         return "k_accumulate_window", 1, n * 2 * c + 4 * N   # all n microbatches, one accumulator write
 
-    def time_mode(self, mode: str, n: int, groups=None) -> dict:
-        """Warm up, then time exactly `steps` steps, with no events, by the
-        wall clock between two device synchronisations.  Then event_steps
-        further steps with a HIP event pair on the launch stream around every
-        call give the per-kernel durations and the per-step spread."""
+    def time_mode(self, mode: str, n: int, groups=None, warmup=None) -> dict:
+        """Warm up (`warmup` steps, default the command line's), then time
+        exactly `steps` steps, with no events, by the wall clock between two
+        device synchronisations.  Then event_steps further steps with a HIP
+        event pair on the launch stream around every call give the per-kernel
+        durations and the per-step spread."""
         torch, args = self.torch, self.args
         ev = {"k_accumulate": [], "k_accumulate_window": [], "k_accumulate_group": [], "k_norm_final": [],
               "k_adamw": []}
-        for _ in range(args.warmup):
+        for _ in range(args.warmup if warmup is None else warmup):
             self.one_step(mode, n, None, groups)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -597,6 +598,12 @@ def _summary(r: dict, note: str) -> dict:
             "roofline_kernel": dom, "roofline_frac": r["kernels"][dom]["frac"], "kernels": r["kernels"]}
 
 
+# Steps of a freshly set-up 1B-shard plan run about 5 % slower for the
+# first ~10 steps (measured: 2.06 ms, then 1.95-1.96 ms per window-call
+# step), so its entry warms up at least this many steps per step kind.
+MIN_WARMUP_1B = 20
+
+
 def dense_1b_entry(args, log, flush_buf) -> dict:
     """The 1B-class dense model's FSDP flat shard (one GPU's eighth, R = 2
     replica slots): full window of 8 and the trailing window of 3, each with
@@ -606,13 +613,14 @@ def dense_1b_entry(args, log, flush_buf) -> dict:
     w = synth.dense_1b_shard()
     full, trailing = w.windows
     t = StepTimer(w, args, log, full, flush_buf)
+    warm = max(args.warmup, MIN_WARMUP_1B)
     out = {"workload": f"{w.name}: {SHAPES[w.name]}, {w.numel} params, R={w.R} stacked replica slots, "
                        f"buckets of {w.bucket_elems} elements, windows {w.windows}, clip {w.max_norm}, "
                        f"AdamW with BF16 parameter copy",
-           "params": w.numel, "R": w.R, "windows": list(w.windows)}
+           "params": w.numel, "R": w.R, "windows": list(w.windows), "steps": args.steps, "warmup": warm}
     for n, label in ((full, "full_window"), (trailing, "trailing_window")):
-        wnd = t.time_mode("window", n)
-        mb = t.time_mode("microbatch", n)
+        wnd = t.time_mode("window", n, warmup=warm)
+        mb = t.time_mode("microbatch", n, warmup=warm)
         out[label] = {
             "window": n,
             "window_call": _summary(wnd, f"one gro_accumulate_window call over the {n} resident microbatches"),
