@@ -66,6 +66,9 @@ def parse():
                     help="skip the streaming probes that measure what each kernel's access pattern can reach")
     ap.add_argument("--no-1b", action="store_true",
                     help="with the draft-67m workload, skip the 1B-shard entry (windows 8 and 3)")
+    ap.add_argument("--only-1b-entry", action="store_true",
+                    help="print only the 1B-shard entry as one JSON line (bench.py runs itself this way in a "
+                         "child process, so that the entry's buffers are the first the process allocates)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the benchmark, run a plain device copy of this many MiB three times "
                          "(the calibration kernel for rocprofv3 byte counters)")
@@ -646,6 +649,14 @@ def main():
     log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
 
     from gradient_reduction_optimizer_amd import synth
+    if args.only_1b_entry:
+        import torch
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        torch.cuda.set_device(0)
+        flush_buf = (torch.ones(args.flush_mib << 18, dtype=torch.float32, device="cuda:0")
+                     if args.flush_mib else None)
+        print(json.dumps(dense_1b_entry(args, log, flush_buf)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]()
     # The oracle's timing forks worker processes, so it runs before this
     # process touches the GPU.
@@ -742,9 +753,31 @@ def main():
         del src, dst
     if w.name == "draft-67m" and not args.no_1b:
         del t
+        flush_buf = None
         torch.cuda.empty_cache()
-        out["dense_1b_shard"] = dense_1b_entry(args, log, flush_buf)
+        out["dense_1b_shard"] = dense_1b_child(args, log)
     print(json.dumps(out), flush=True)
+
+
+def dense_1b_child(args, log) -> dict:
+    """The 1B-shard entry measured by this script in a child process.  In a
+    process that has already allocated and freed other buffers the 1B step
+    measured 1-3 % slower than in a fresh one (1.977 and 2.011 ms against
+    1.956 ms per window-call step); a training job allocates its buffers
+    once at start, so the fresh process is the representative one."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--only-1b-entry", "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--flush-mib", str(args.flush_mib)]
+    if args.no_probe:
+        cmd.append("--no-probe")
+    if args.quiet:
+        cmd.append("--quiet")
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"the 1B-shard entry's process failed with exit code {r.returncode}")
+    entry = json.loads(r.stdout.strip().splitlines()[-1])
+    entry["process"] = "measured in a child process of bench.py (its first device allocations)"
+    return entry
 
 
 if __name__ == "__main__":
