@@ -66,6 +66,9 @@ def parse():
                     help="skip the streaming probes that measure what each kernel's access pattern can reach")
     ap.add_argument("--no-1b", action="store_true",
                     help="with the draft-67m workload, skip the 1B-shard entry (windows 8 and 3)")
+    ap.add_argument("--lib", default=None,
+                    help="time this build of libgro.so instead of the in-tree one (a variant from "
+                         "`python -m gradient_reduction_optimizer_amd.build --variant`)")
     ap.add_argument("--only-1b-entry", action="store_true",
                     help="print only the 1B-shard entry as one JSON line (bench.py runs itself this way in a "
                          "child process, so that the entry's buffers are the first the process allocates)")
@@ -163,6 +166,11 @@ def pattern_probes(st, n_micro: int, c_mix: int, N: int, flush, stream, log, rep
         log(f"pattern probe {name}: 4 per lane " + ", ".join(
             f"{key} {val:.0f}" for key, val in res[name].items() if key != "wide") + "; 8 per lane " +
             ", ".join(f"{key} {val:.0f}" for key, val in res[name]["wide"].items()))
+    # Plain streams over the same arrays and chunking, for scale: what reading
+    # only, writing only and copying reach at this size (back to back).
+    res["reference_streams"] = {"read_only": run(6, 0, 4, False), "write_only": run(7, 0, 4, False),
+                                "copy": run(8, 0, 8, False)}
+    log("reference streams: " + ", ".join(f"{k} {v:.0f}" for k, v in res["reference_streams"].items()))
     del g
     torch.cuda.empty_cache()
     return res
@@ -647,6 +655,11 @@ def main():
               f"(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     log = (lambda *a: None) if args.quiet else (lambda *a: print(*a, file=sys.stderr, flush=True))
+    if args.lib:
+        from gradient_reduction_optimizer_amd import binding
+        if not os.path.exists(args.lib):
+            raise SystemExit(f"--lib {args.lib}: no such library")
+        binding.LIB_PATH = os.path.abspath(args.lib)
 
     from gradient_reduction_optimizer_amd import synth
     if args.only_1b_entry:
@@ -702,7 +715,8 @@ def main():
                                f"(every microbatch's BF16 gradient buckets resident), global norm, "
                                f"clip {w.max_norm}, AdamW with BF16 parameter copy",
                    "params": w.numel, "R": w.R, "window": n, "bucket_elems": w.bucket_elems,
-                   "n_buckets": t.nb, "n_chunks": t.info["n_chunks"], "parallelism": "single GPU share"},
+                   "n_buckets": t.nb, "n_chunks": t.info["n_chunks"], "parallelism": "single GPU share",
+                   "library": os.path.relpath(args.lib, ROOT) if args.lib else "in-tree libgro.so"},
         "step_hbm": wnd["step_hbm"],
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": load_traffic(dom, w.name)},
@@ -770,6 +784,8 @@ def dense_1b_child(args, log) -> dict:
            "--warmup", str(args.warmup), "--flush-mib", str(args.flush_mib)]
     if args.no_probe:
         cmd.append("--no-probe")
+    if args.lib:
+        cmd += ["--lib", args.lib]
     if args.quiet:
         cmd.append("--quiet")
     r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)

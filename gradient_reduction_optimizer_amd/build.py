@@ -2,6 +2,7 @@
 probes for the benchmark) in-tree for gfx950.
 
     python -m gradient_reduction_optimizer_amd.build
+    python -m gradient_reduction_optimizer_amd.build --variant NAME [DEFINE=VALUE ...]
 
 The planner is plain C++ (g++); the device entry points and kernels are HIP
 (hipcc, gfx950 only).  No contraction of FP operations anywhere, so each
@@ -68,6 +69,30 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+VARIANTS = os.path.join(BUILD, "variants")
+
+
+def build_variant(name: str, defines, verbose: bool = False) -> str:
+    """Build libgro.so with compile-time knobs (e.g. ["GRO_UNROLL_WIN=4"]) as
+    _build/variants/libgro_<name>.so, for launch-shape comparisons with
+    `bench.py --lib`.  The in-tree libgro.so is not touched."""
+    os.makedirs(VARIANTS, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
+    objs = []
+    o = os.path.join(VARIANTS, f"{name}_plan.o")
+    _run(["g++", *COMMON, *dflags, "-c", os.path.join(CSRC, "plan.cpp"), "-o", o], verbose)
+    objs.append(o)
+    for src in ("kernels", "abi"):
+        o = os.path.join(VARIANTS, f"{name}_{src}.o")
+        _run([HIPCC, *COMMON, *HIP_FLAGS, *dflags, "-c", os.path.join(CSRC, f"{src}.hip"), "-o", o], verbose)
+        objs.append(o)
+    out = os.path.join(VARIANTS, f"libgro_{name}.so")
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out], verbose)
+    for o in objs:
+        os.remove(o)
+    return out
+
+
 def device_asm(out_path: str) -> str:
     """Write the gfx950 assembly of the kernels (for inspection)."""
     _run([HIPCC, *COMMON, *HIP_FLAGS, "--cuda-device-only", "-S",
@@ -76,4 +101,8 @@ def device_asm(out_path: str) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if len(sys.argv) >= 3 and sys.argv[1] == "--variant":
+        # python -m gradient_reduction_optimizer_amd.build --variant NAME [DEFINE=VALUE ...]
+        print(build_variant(sys.argv[2], sys.argv[3:]))
+    else:
+        print(build(verbose="-v" in sys.argv))

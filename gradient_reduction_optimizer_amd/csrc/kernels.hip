@@ -57,6 +57,10 @@ constexpr int kWaves = kBlock / 64;
 #ifndef GRO_UNROLL_WIN
 #define GRO_UNROLL_WIN GRO_UNROLL
 #endif
+// 1: the window pass stores the accumulator with the non-temporal policy.
+#ifndef GRO_WIN_ACC_NT
+#define GRO_WIN_ACC_NT 0
+#endif
 // Window lengths up to this many microbatches issue every microbatch's loads
 // at once (window_full_n); longer ones pipeline microbatch by microbatch.
 #ifndef GRO_WIN_ALL_AT_ONCE
@@ -413,6 +417,10 @@ struct WinChunk {
   Divisor rdiv;
   Divisor wdiv;
   __device__ const void* g(int k) const { return P->grads[k * P->n_buckets + j]; }
+  __device__ void store_acc(int64_t e, const f32x4 x) const {
+    if (GRO_WIN_ACC_NT) st4f_nt(acc + e, x);
+    else st4f(acc + e, x);
+  }
 };
 
 template <typename In>
@@ -444,7 +452,7 @@ __device__ double window_generic(const WinChunk& c) {
       }
       acc = (c.first && k == 0) ? red : acc + red;
     }
-    st4f(c.acc + 4 * v, acc);
+    c.store_acc(4 * v, acc);
     if (c.fuse) {
       ss += sq(divide(acc.x, c.wdiv));
       ss += sq(divide(acc.y, c.wdiv));
@@ -512,7 +520,7 @@ __device__ double window_full(const WinChunk& c) {
     }
 #pragma unroll
     for (int u = 0; u < kUnrollWin; ++u) {
-      st4f(c.acc + 4 * (v0 + u * kBlock), acc[u]);
+      c.store_acc(4 * (v0 + u * kBlock), acc[u]);
       if (WM != kNoDiv) {
         ss += sq(divide_m<WM>(acc[u].x, c.wdiv));
         ss += sq(divide_m<WM>(acc[u].y, c.wdiv));
@@ -555,7 +563,7 @@ __device__ double window_full_n(const WinChunk& c) {
         red.w = divide_m<RM>(red.w, c.rdiv);
         acc = k == 0 ? red : acc + red;
       }
-      st4f(c.acc + 4 * (v0 + u * kBlock), acc);
+      c.store_acc(4 * (v0 + u * kBlock), acc);
       ss += sq(divide_m<WM>(acc.x, c.wdiv));
       ss += sq(divide_m<WM>(acc.y, c.wdiv));
       ss += sq(divide_m<WM>(acc.z, c.wdiv));

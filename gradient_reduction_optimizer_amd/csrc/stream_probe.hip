@@ -23,6 +23,16 @@
 //                               per element; 8 elements per lane in flight.
 // Patterns 0-2 use 4 elements per lane access, 3-5 use 8.
 //
+// Reference streams, the same chunking and 4 elements per lane, default
+// cache policy, to say what plain streaming reaches on this device at the
+// same size:
+//   pattern 6, read only:   read one FP32 stream (p); each workgroup writes
+//                           its first wave's sum, one float (to m).  4 bytes
+//                           per element.
+//   pattern 7, write only:  write one FP32 stream (p).  4 bytes per element.
+//   pattern 8, copy:        read one FP32 stream (acc), write another (p).
+//                           8 bytes per element.
+//
 // Arguments: n elements (a multiple of 4,096); device pointers as the pattern
 // needs them (unused ones may be NULL); for the window patterns `k` BF16
 // stream pointers in `g`, k in 1..8, 12 or 16 (the window kernel reads window
@@ -170,6 +180,36 @@ __global__ __launch_bounds__(kLanes) void probe_accumulate(const Streams s) {
   }
 }
 
+// Reference streams: 16 elements per lane, all loads issued before use.
+__global__ __launch_bounds__(kLanes) void probe_read(const Streams s) {
+  const int64_t base = int64_t(blockIdx.x) * kChunk;
+  f32x4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const f32x4*>(s.p + base + 4 * (threadIdx.x + u * kLanes));
+  f32x4 t = (x[0] + x[1]) + (x[2] + x[3]);
+  float r = (t.x + t.y) + (t.z + t.w);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) r += __shfl_xor(r, m, 64);
+  if (threadIdx.x == 0) s.m[blockIdx.x] = r;  // keeps the loads; 4 bytes written per 4,096 elements
+}
+
+__global__ __launch_bounds__(kLanes) void probe_write(const Streams s) {
+  const int64_t base = int64_t(blockIdx.x) * kChunk;
+  const float b = float(blockIdx.x);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    *reinterpret_cast<f32x4*>(s.p + base + 4 * (threadIdx.x + u * kLanes)) = f32x4{b, b, b, b};
+}
+
+__global__ __launch_bounds__(kLanes) void probe_copy(const Streams s) {
+  const int64_t base = int64_t(blockIdx.x) * kChunk;
+  f32x4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const f32x4*>(s.acc + base + 4 * (threadIdx.x + u * kLanes));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4*>(s.p + base + 4 * (threadIdx.x + u * kLanes)) = x[u];
+}
+
 template <int W>
 hipError_t launch_window(int k, const dim3 grid, const Streams& s, hipStream_t st) {
   const dim3 block(kLanes);
@@ -231,6 +271,18 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
       s.g[0] = g[0];
       if (wide) hipLaunchKernelGGL(probe_accumulate<8>, grid, block, 0, st, s);
       else hipLaunchKernelGGL(probe_accumulate<4>, grid, block, 0, st, s);
+      break;
+    case 6:
+      if (!p || !m) return -1;
+      hipLaunchKernelGGL(probe_read, grid, block, 0, st, s);
+      break;
+    case 7:
+      if (!p) return -1;
+      hipLaunchKernelGGL(probe_write, grid, block, 0, st, s);
+      break;
+    case 8:
+      if (!acc || !p) return -1;
+      hipLaunchKernelGGL(probe_copy, grid, block, 0, st, s);
       break;
     default:
       return -1;

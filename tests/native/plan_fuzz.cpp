@@ -3,8 +3,9 @@
 // Sanitizer by tests/test_plan_sanitizers.py.  Random descriptor sets; for
 // each accepted plan it checks the layout invariants (disjoint, aligned,
 // capacity-bounded buckets; chunks partitioning every bucket; every updated
-// element in exactly one tensor span) and that rejected plans return a
-// GRO_E_* code with a message.  Exit status 0 = all checks held.
+// element in exactly one tensor span; a workspace large enough for every
+// device table) and that rejected plans return a GRO_E_* code with a
+// message.  Exit status 0 = all checks held.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -73,6 +74,13 @@ int main(int argc, char** argv) {
       CHECK(end <= info.n_flat);
     }
     CHECK(q == info.n_chunks && owned == info.n_owned);
+    // the device workspace holds the scalars, the bucket and chunk tables,
+    // one FP64 partial per chunk, the init table, one FP64 sum per group of
+    // 2,048 partials and a uint32 counter per group plus one
+    const uint64_t groups = uint64_t((info.n_chunks + 2047) / 2048);
+    CHECK(info.workspace_bytes % 256 == 0);
+    CHECK(info.workspace_bytes >= 256 + 32 * uint64_t(info.n_buckets) + 24 * uint64_t(info.n_chunks) +
+                                      48 * uint64_t(info.n_tensors) + 8 * groups + 4 * (groups + 1));
     int64_t spans = 0;
     for (int32_t i = 0; i < n; ++i) {
       gro_tensor_layout t;

@@ -56,6 +56,25 @@ def test_probe_patterns_compute_what_they_read(lib, wide):
     assert torch.equal(pb.view(torch.int16), (p.view(torch.int32) >> 16).to(torch.int16))
 
 
+def test_reference_streams_compute_what_they_read(lib):
+    """Patterns 6-8: read-only (one sum per workgroup), write-only, copy."""
+    n = 3 * 4096
+    s = torch.cuda.current_stream().cuda_stream
+    src, dst, sums = _rand(n, 31), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    assert lib.gro_probe_stream(8, n, src.data_ptr(), dst.data_ptr(), None, None, None, None, 0, s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    assert lib.gro_probe_stream(7, n, None, dst.data_ptr(), None, None, None, None, 0, s) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst, torch.arange(3, device="cuda").float().repeat_interleave(4096))
+    x = torch.ones(n, device="cuda")
+    assert lib.gro_probe_stream(6, n, None, x.data_ptr(), sums.data_ptr(), None, None, None, 0, s) == 0
+    torch.cuda.synchronize()
+    # each workgroup's first wave: 64 lanes x 16 elements
+    assert torch.equal(sums[:3], torch.full((3,), 1024.0, device="cuda"))
+    assert lib.gro_probe_stream(6, n, None, x.data_ptr(), None, None, None, None, 0, s) == -1
+
+
 def test_probe_rejects_bad_arguments(lib):
     s = torch.cuda.current_stream().cuda_stream
     out = torch.zeros(8192, device="cuda")
@@ -66,4 +85,4 @@ def test_probe_rejects_bad_arguments(lib):
     assert lib.gro_probe_stream(1, 8192, None, out.data_ptr(), None, None, None, gp, 17, s) == -1
     assert lib.gro_probe_stream(0, 8192, None, out.data_ptr(), None, None, None, None, 0, s) == -1  # missing arrays
     assert lib.gro_probe_stream(4, 8192, None, out.data_ptr(), None, None, None, gp, 9, s) == -1  # k not built
-    assert lib.gro_probe_stream(7, 8192, None, out.data_ptr(), None, None, None, gp, 1, s) == -1  # no such pattern
+    assert lib.gro_probe_stream(9, 8192, None, out.data_ptr(), None, None, None, gp, 1, s) == -1  # no such pattern
