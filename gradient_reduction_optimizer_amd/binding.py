@@ -96,6 +96,14 @@ def load() -> ctypes.CDLL:
             _build.build()
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gradient_reduction_optimizer_amd.build`")
+    # PyTorch ships its own HIP runtime under the same library name.  Load it
+    # first, so that libgro.so binds to the runtime PyTorch uses: with the
+    # system one loaded first, two runtimes would own the device in one
+    # process and device calls fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, U64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
     L.gro_plan_create.argtypes = [ctypes.POINTER(gro_tensor_desc), I32, I32, I64, ctypes.POINTER(P)]

@@ -103,6 +103,29 @@ int check_window_acc(const gro_plan* p, int32_t b0, int32_t b1, const float* d_a
   return GRO_OK;
 }
 
+// Accumulator store policy of the window pass (GRO_WIN_ACC_NT) and of the
+// per-microbatch pass (GRO_MB_ACC_NT).  The accumulator is read next by the
+// following pass or by AdamW, which walks the chunks in reverse to meet the
+// last-written ones in the 256 MB memory-side Infinity Cache.  That pays
+// while the accumulator is about the cache's size; accumulators several
+// times larger are stored non-temporally (they cannot stay in the cache and
+// would otherwise churn it on their way to HBM), which measured faster.
+// Knobs: 0 never, 1 always, 2 when the accumulator is larger than
+// GRO_ACC_NT_BYTES.
+#ifndef GRO_WIN_ACC_NT
+#define GRO_WIN_ACC_NT 2
+#endif
+#ifndef GRO_MB_ACC_NT
+#define GRO_MB_ACC_NT 2
+#endif
+#ifndef GRO_ACC_NT_BYTES
+#define GRO_ACC_NT_BYTES (512ll << 20)
+#endif
+bool acc_nontemporal(const gro_plan* p, int knob) {
+  if (knob == 2) return p->n_flat * int64_t(sizeof(float)) > GRO_ACC_NT_BYTES;
+  return knob == 1;
+}
+
 void reset_window(gro_plan* p) {
   std::fill(p->count.begin(), p->count.end(), 0);
   std::fill(p->partials_ready.begin(), p->partials_ready.end(), 0);
@@ -230,6 +253,7 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
     a.micro_index = micro_index;
     a.fuse_norm = fuse ? 1 : 0;
     a.window = window_size;
+    a.acc_nt = acc_nontemporal(p, GRO_MB_ACC_NT) ? 1 : 0;
     const hipError_t e = launch_accumulate(a, s);
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   }
@@ -310,6 +334,7 @@ int accumulate_group(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_g
         a.grads[k * (le - lb) + (b - lb)] = d_grad_buckets[int64_t(k) * span + (b - b0)];
     a.acc = d_acc;
     a.partials = dev_partials(p);
+    a.acc_nt = acc_nontemporal(p, GRO_WIN_ACC_NT) ? 1 : 0;
     const hipError_t e = launch_accumulate_window(a, s);
     if (e != hipSuccess) return hip_fail(e, "accumulate-window launch");
   }

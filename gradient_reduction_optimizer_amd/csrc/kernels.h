@@ -25,6 +25,7 @@ struct AccumulateLaunch {
   int32_t micro_index;
   int32_t fuse_norm;
   int32_t window;           // microbatches in the window (used when fuse_norm)
+  int32_t acc_nt;           // 1: store the accumulator with the non-temporal policy
 };
 
 // A whole accumulation window in one pass: grads[k * n_buckets + j] is
@@ -40,6 +41,7 @@ struct WindowLaunch {
   int32_t first;            // 1: the group opens the window (accumulator overwritten)
   int32_t fuse_norm;        // 1: the group closes the window (norm partials written)
   int32_t window;           // microbatches in the whole window (the norm's divisor)
+  int32_t acc_nt;           // 1: store the accumulator with the non-temporal policy
   const void* grads[kMaxBucketsPerLaunch];
   float* acc;
   double* partials;

@@ -57,10 +57,6 @@ constexpr int kWaves = kBlock / 64;
 #ifndef GRO_UNROLL_WIN
 #define GRO_UNROLL_WIN GRO_UNROLL
 #endif
-// 1: the window pass stores the accumulator with the non-temporal policy.
-#ifndef GRO_WIN_ACC_NT
-#define GRO_WIN_ACC_NT 0
-#endif
 // Window lengths up to this many microbatches issue every microbatch's loads
 // at once (window_full_n); longer ones pipeline microbatch by microbatch.
 #ifndef GRO_WIN_ALL_AT_ONCE
@@ -155,6 +151,14 @@ __device__ __forceinline__ void st4f_nt(float* p, const f32x4 v) {
 }
 __device__ __forceinline__ void st2u_nt(uint16_t* p, const u32x2 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+}
+// An accumulator store with the policy fixed at compile time (a run-time
+// choice between the two stores is merged into one plain store by the
+// compiler).
+template <bool NT>
+__device__ __forceinline__ void st4f_acc(float* p, const f32x4 v) {
+  if constexpr (NT) st4f_nt(p, v);
+  else st4f(p, v);
 }
 
 // Sum over the workgroup in a fixed order: a wave64 butterfly (every lane
@@ -311,7 +315,7 @@ __device__ double accumulate_generic(const AccChunk& c) {
 // R = 2), FIRST whether the window starts here, WM the window division for
 // the fused norm (kNoDiv = no norm).  Same operations, same order as
 // accumulate_generic, without bounds checks or per-element branches.
-template <typename In, int C, int RM, bool FIRST, int WM>
+template <typename In, int C, int RM, bool FIRST, int WM, bool NT>
 __device__ double accumulate_full(const AccChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   double ss = 0.0;
@@ -339,7 +343,7 @@ __device__ double accumulate_full(const AccChunk& c) {
       s.z = divide_m<RM>(s.z, c.rdiv);
       s.w = divide_m<RM>(s.w, c.rdiv);
       if (!FIRST) s = old[u] + s;
-      st4f(c.acc + 4 * v, s);
+      st4f_acc<NT>(c.acc + 4 * v, s);
       if (WM != kNoDiv) {
         ss += sq(divide_m<WM>(s.x, c.wdiv));
         ss += sq(divide_m<WM>(s.y, c.wdiv));
@@ -351,27 +355,30 @@ __device__ double accumulate_full(const AccChunk& c) {
   return ss;
 }
 
-template <typename In, int C, int RM>
+template <typename In, int C, int RM, bool NT>
 __device__ double accumulate_full_dispatch(const AccChunk& c) {
   const int wm = c.fuse ? div_mode(c.wdiv) : kNoDiv;
   if (c.first) {
-    if (wm == kNoDiv) return accumulate_full<In, C, RM, true, kNoDiv>(c);
-    if (wm == kMulInv) return accumulate_full<In, C, RM, true, kMulInv>(c);
-    return accumulate_full<In, C, RM, true, kIeeeDiv>(c);
+    if (wm == kNoDiv) return accumulate_full<In, C, RM, true, kNoDiv, NT>(c);
+    if (wm == kMulInv) return accumulate_full<In, C, RM, true, kMulInv, NT>(c);
+    return accumulate_full<In, C, RM, true, kIeeeDiv, NT>(c);
   }
-  if (wm == kNoDiv) return accumulate_full<In, C, RM, false, kNoDiv>(c);
-  if (wm == kMulInv) return accumulate_full<In, C, RM, false, kMulInv>(c);
-  return accumulate_full<In, C, RM, false, kIeeeDiv>(c);
+  if (wm == kNoDiv) return accumulate_full<In, C, RM, false, kNoDiv, NT>(c);
+  if (wm == kMulInv) return accumulate_full<In, C, RM, false, kMulInv, NT>(c);
+  return accumulate_full<In, C, RM, false, kIeeeDiv, NT>(c);
 }
 
-template <typename In>
+template <typename In, bool NT>
 __device__ double accumulate_chunk(const AccChunk& c) {
-  if (c.len == kChunkElems && c.slots == 1 && !c.mean) return accumulate_full_dispatch<In, 1, kNoDiv>(c);
-  if (c.len == kChunkElems && c.slots == 2 && !c.mean) return accumulate_full_dispatch<In, 2, kNoDiv>(c);
-  if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2) return accumulate_full_dispatch<In, 2, kMulInv>(c);
+  if (c.len == kChunkElems && c.slots == 1 && !c.mean) return accumulate_full_dispatch<In, 1, kNoDiv, NT>(c);
+  if (c.len == kChunkElems && c.slots == 2 && !c.mean) return accumulate_full_dispatch<In, 2, kNoDiv, NT>(c);
+  if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2) return accumulate_full_dispatch<In, 2, kMulInv, NT>(c);
   return accumulate_generic<In>(c);
 }
 
+// NT: full chunks store the accumulator non-temporally (one kernel per
+// policy, chosen by the launcher).
+template <bool NT>
 __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P) {
   const int64_t q = chunk_of_block(P.q_begin);
   if (q < P.q_begin || q >= P.q_end) return;
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void k_accumulate(const AccumulateLaunch P)
   c.fuse = P.fuse_norm != 0;
   c.rdiv = make_divisor(P.R);
   c.wdiv = make_divisor(P.window > 0 ? P.window : 1);
-  const double ss = bk.grad_fp32 ? accumulate_chunk<F32In>(c) : accumulate_chunk<Bf16In>(c);
+  const double ss = bk.grad_fp32 ? accumulate_chunk<F32In, NT>(c) : accumulate_chunk<Bf16In, NT>(c);
   if (c.fuse) {
     const double t = block_sum(ss);
     if (threadIdx.x == 0) P.partials[q] = t;
@@ -417,10 +424,6 @@ struct WinChunk {
   Divisor rdiv;
   Divisor wdiv;
   __device__ const void* g(int k) const { return P->grads[k * P->n_buckets + j]; }
-  __device__ void store_acc(int64_t e, const f32x4 x) const {
-    if (GRO_WIN_ACC_NT) st4f_nt(acc + e, x);
-    else st4f(acc + e, x);
-  }
 };
 
 template <typename In>
@@ -452,7 +455,7 @@ __device__ double window_generic(const WinChunk& c) {
       }
       acc = (c.first && k == 0) ? red : acc + red;
     }
-    c.store_acc(4 * v, acc);
+    st4f(c.acc + 4 * v, acc);
     if (c.fuse) {
       ss += sq(divide(acc.x, c.wdiv));
       ss += sq(divide(acc.y, c.wdiv));
@@ -475,7 +478,7 @@ __device__ double window_generic(const WinChunk& c) {
 // mode WM (kNoDiv: no norm partial) and FIRST (the group opens the window)
 // fixed at compile time, any number of microbatches.  Microbatch k+1's loads
 // are issued before microbatch k's data is consumed.
-template <typename In, int C, int RM, int WM, bool FIRST>
+template <typename In, int C, int RM, int WM, bool FIRST, bool NT>
 __device__ double window_full(const WinChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   const int n = c.P->n_micro;
@@ -520,7 +523,7 @@ __device__ double window_full(const WinChunk& c) {
     }
 #pragma unroll
     for (int u = 0; u < kUnrollWin; ++u) {
-      c.store_acc(4 * (v0 + u * kBlock), acc[u]);
+      st4f_acc<NT>(c.acc + 4 * (v0 + u * kBlock), acc[u]);
       if (WM != kNoDiv) {
         ss += sq(divide_m<WM>(acc[u].x, c.wdiv));
         ss += sq(divide_m<WM>(acc[u].y, c.wdiv));
@@ -534,7 +537,7 @@ __device__ double window_full(const WinChunk& c) {
 
 // Common window lengths: every microbatch's loads are issued before any
 // is consumed (N * C * kUnrollWin loads in flight per lane).
-template <typename In, int C, int RM, int WM, int N>
+template <typename In, int C, int RM, int WM, int N, bool NT>
 __device__ double window_full_n(const WinChunk& c) {
   constexpr int nvec = kChunkElems / 4;
   double ss = 0.0;
@@ -563,7 +566,7 @@ __device__ double window_full_n(const WinChunk& c) {
         red.w = divide_m<RM>(red.w, c.rdiv);
         acc = k == 0 ? red : acc + red;
       }
-      c.store_acc(4 * (v0 + u * kBlock), acc);
+      st4f_acc<NT>(c.acc + 4 * (v0 + u * kBlock), acc);
       ss += sq(divide_m<WM>(acc.x, c.wdiv));
       ss += sq(divide_m<WM>(acc.y, c.wdiv));
       ss += sq(divide_m<WM>(acc.z, c.wdiv));
@@ -573,38 +576,40 @@ __device__ double window_full_n(const WinChunk& c) {
   return ss;
 }
 
-template <typename In, int C, int RM, int WM>
+template <typename In, int C, int RM, int WM, bool NT>
 __device__ double window_full_w(const WinChunk& c) {
   // FP32 contributions take twice the registers: keep them double-buffered.
-  if (sizeof(typename In::raw_t) > 8) return window_full<In, C, RM, WM, true>(c);
+  if (sizeof(typename In::raw_t) > 8) return window_full<In, C, RM, WM, true, NT>(c);
   const int n = c.P->n_micro;
-  if (n > GRO_WIN_ALL_AT_ONCE) return window_full<In, C, RM, WM, true>(c);
+  if (n > GRO_WIN_ALL_AT_ONCE) return window_full<In, C, RM, WM, true, NT>(c);
   switch (n) {
-    case 2: return window_full_n<In, C, RM, WM, 2>(c);
-    case 3: return window_full_n<In, C, RM, WM, 3>(c);
-    case 4: return window_full_n<In, C, RM, WM, 4>(c);
-    case 8: return window_full_n<In, C, RM, WM, 8>(c);
-    default: return window_full<In, C, RM, WM, true>(c);
+    case 2: return window_full_n<In, C, RM, WM, 2, NT>(c);
+    case 3: return window_full_n<In, C, RM, WM, 3, NT>(c);
+    case 4: return window_full_n<In, C, RM, WM, 4, NT>(c);
+    case 8: return window_full_n<In, C, RM, WM, 8, NT>(c);
+    default: return window_full<In, C, RM, WM, true, NT>(c);
   }
 }
 
-template <typename In, int C, int RM>
+template <typename In, int C, int RM, bool NT>
 __device__ double window_full_dispatch(const WinChunk& c) {
   if (c.first && c.fuse)  // a whole window in one pass
-    return c.wdiv.pow2 ? window_full_w<In, C, RM, kMulInv>(c) : window_full_w<In, C, RM, kIeeeDiv>(c);
+    return c.wdiv.pow2 ? window_full_w<In, C, RM, kMulInv, NT>(c) : window_full_w<In, C, RM, kIeeeDiv, NT>(c);
   // a group of microbatches inside a window
-  if (!c.fuse) return c.first ? window_full<In, C, RM, kNoDiv, true>(c) : window_full<In, C, RM, kNoDiv, false>(c);
-  return c.wdiv.pow2 ? window_full<In, C, RM, kMulInv, false>(c) : window_full<In, C, RM, kIeeeDiv, false>(c);
+  if (!c.fuse)
+    return c.first ? window_full<In, C, RM, kNoDiv, true, NT>(c) : window_full<In, C, RM, kNoDiv, false, NT>(c);
+  return c.wdiv.pow2 ? window_full<In, C, RM, kMulInv, false, NT>(c) : window_full<In, C, RM, kIeeeDiv, false, NT>(c);
 }
 
-template <typename In>
+template <typename In, bool NT>
 __device__ double window_chunk(const WinChunk& c) {
-  if (c.len == kChunkElems && c.slots == 1 && !c.mean) return window_full_dispatch<In, 1, kNoDiv>(c);
-  if (c.len == kChunkElems && c.slots == 2 && !c.mean) return window_full_dispatch<In, 2, kNoDiv>(c);
-  if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2) return window_full_dispatch<In, 2, kMulInv>(c);
+  if (c.len == kChunkElems && c.slots == 1 && !c.mean) return window_full_dispatch<In, 1, kNoDiv, NT>(c);
+  if (c.len == kChunkElems && c.slots == 2 && !c.mean) return window_full_dispatch<In, 2, kNoDiv, NT>(c);
+  if (c.len == kChunkElems && c.slots == 2 && c.rdiv.pow2) return window_full_dispatch<In, 2, kMulInv, NT>(c);
   return window_generic<In>(c);
 }
 
+template <bool NT>
 __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch P) {
   const int64_t q = window_chunk_of_block(P.q_begin, P.q_end);
   if (q < P.q_begin || q >= P.q_end) return;
@@ -623,7 +628,7 @@ __global__ __launch_bounds__(kBlock) void k_accumulate_window(const WindowLaunch
   c.fuse = P.fuse_norm != 0;
   c.rdiv = make_divisor(P.R);
   c.wdiv = make_divisor(P.window > 0 ? P.window : 1);
-  const double ss = bk.grad_fp32 ? window_chunk<F32In>(c) : window_chunk<Bf16In>(c);
+  const double ss = bk.grad_fp32 ? window_chunk<F32In, NT>(c) : window_chunk<Bf16In, NT>(c);
   if (c.fuse) {
     const double t = block_sum(ss);
     if (threadIdx.x == 0) P.partials[q] = t;
@@ -986,7 +991,8 @@ hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s) {
 hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
   const int64_t blocks = (a.q_end - a.q_begin) + (a.q_begin & 7);
-  hipLaunchKernelGGL(k_accumulate, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  if (a.acc_nt) hipLaunchKernelGGL(k_accumulate<true>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL(k_accumulate<false>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -994,7 +1000,8 @@ hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
   const int64_t blocks = GRO_WIN_MAP == 0 ? (a.q_end - a.q_begin) + (a.q_begin & 7)
                                           : ((a.q_end - a.q_begin + 7) >> 3) * 8;
-  hipLaunchKernelGGL(k_accumulate_window, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  if (a.acc_nt) hipLaunchKernelGGL(k_accumulate_window<true>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL(k_accumulate_window<false>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
