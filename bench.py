@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of the workload's elements the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-cpu-baseline", action="store_true",
+                    help="print only the CPU oracle's timing as one JSON line, without touching the GPU "
+                         "(bench.py runs itself this way in a child process)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024,
                     help="size of the buffer read before every call in the cold-cache timing (0: skip it)")
@@ -671,9 +674,9 @@ def main():
         print(json.dumps(dense_1b_entry(args, log, flush_buf)), flush=True)
         return
     w = synth.WORKLOADS[args.workload]()
-    # The oracle's timing forks worker processes, so it runs before this
-    # process touches the GPU.
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_sample_frac, log)
+    if args.only_cpu_baseline:
+        print(json.dumps(cpu_baseline(w, args.cpu_sample_frac, log)), flush=True)
+        return
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -753,8 +756,6 @@ def main():
             if "cold_cache" in out and att[dom].get("GBps_cold"):
                 ck = out["cold_cache"]["window_call"]["kernels"][dom]
                 ck["frac_of_pattern_probe"] = ck["GBps"] / att[dom]["GBps_cold"]
-    if cpu is not None:
-        out["cpu_baseline"] = cpu
     if args.copy_probe_mib:
         nbytes = args.copy_probe_mib << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
@@ -770,7 +771,29 @@ def main():
         flush_buf = None
         torch.cuda.empty_cache()
         out["dense_1b_shard"] = dense_1b_child(args, log)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_child(args, log)
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_child(args, log) -> dict:
+    """cpu_baseline in a child process (`bench.py --only-cpu-baseline`),
+    after the GPU timing.  Run inside this process before the GPU timing, the
+    oracle's gigabytes of host arrays and its forked workers left the host
+    slow to issue the first timed calls: the per-call events of the
+    draft-67m per-microbatch steps then read 440-590 us per 90 us launch
+    (the wall clock of the timed steps was unchanged)."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--only-cpu-baseline", "--workload", args.workload,
+           "--cpu-sample-frac", str(args.cpu_sample_frac)]
+    if args.quiet:
+        cmd.append("--quiet")
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"the CPU baseline's process failed with exit code {r.returncode}")
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    out["process"] = "timed in a child process of bench.py after the GPU timing (no GPU use)"
+    return out
 
 
 def dense_1b_child(args, log) -> dict:

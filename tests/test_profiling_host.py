@@ -2,6 +2,7 @@
 handling (no GPU needed).  The CSV rows below are hand-made fixtures in
 rocprofv3's column layout, not measurements."""
 import csv
+import json
 import os
 import subprocess
 import sys
@@ -83,6 +84,17 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_bench_times_the_cpu_oracle_without_the_gpu():
+    """The CPU baseline's own mode (the child process bench.py starts after
+    its GPU timing) prints one JSON line and touches no GPU."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--only-cpu-baseline", "--workload",
+                        "tiny-literal", "--quiet"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert out["kind"] == "oracle" and out["bit_identical_across_core_counts"] is True
+    assert out["one_core"]["cores"] == 1 and out["value"] > 0
 
 
 def test_exact_sum_of_squares_matches_a_correctly_rounded_sum():
