@@ -126,6 +126,42 @@ bool acc_nontemporal(const gro_plan* p, int knob) {
   return knob == 1;
 }
 
+// Workgroups per CU of the accumulate passes.  Far beyond the Infinity
+// Cache each workgroup keeps every one of its input streams open in HBM at
+// once; fewer workgroups sharing a CU measured faster there, the more so
+// the more streams a pass reads: at most 2 per CU for a window pass of 12
+// or more streams (8 microbatches of 2 slots), 3 for 5 to 11, and 3 for
+// the per-microbatch pass.  On accumulators within a few times the cache
+// (draft-67m-sized plans) and on window passes of 1-4 streams all of them
+// stay, which measured faster.  The cap is a launch parameter, not a
+// kernel argument: results are unchanged.
+// Knobs: GRO_WG_CAP 0 never capped, 1 the rule above on every plan, 2 on
+// accumulators larger than GRO_ACC_NT_BYTES; GRO_WIN_WG / GRO_MB_WG > 0
+// force that cap on every window / per-microbatch pass, -1 none.
+#ifndef GRO_WG_CAP
+#define GRO_WG_CAP 2
+#endif
+#ifndef GRO_WIN_WG
+#define GRO_WIN_WG 0
+#endif
+#ifndef GRO_MB_WG
+#define GRO_MB_WG 0
+#endif
+bool wg_capped(const gro_plan* p) {
+  if (GRO_WG_CAP == 2) return p->n_flat * int64_t(sizeof(float)) > GRO_ACC_NT_BYTES;
+  return GRO_WG_CAP == 1;
+}
+size_t window_lds(const gro_plan* p, int32_t streams) {
+  int32_t cap = GRO_WIN_WG;
+  if (cap == 0) cap = !wg_capped(p) ? 0 : streams >= 12 ? 2 : streams >= 5 ? 3 : 0;
+  return wg_cap_lds_bytes(cap, p->max_lds_per_block);
+}
+size_t micro_lds(const gro_plan* p) {
+  int32_t cap = GRO_MB_WG;
+  if (cap == 0) cap = wg_capped(p) ? 3 : 0;
+  return wg_cap_lds_bytes(cap, p->max_lds_per_block);
+}
+
 void reset_window(gro_plan* p) {
   std::fill(p->count.begin(), p->count.end(), 0);
   std::fill(p->partials_ready.begin(), p->partials_ready.end(), 0);
@@ -160,6 +196,10 @@ int bind_to(gro_plan* p, char* ws, void* stream, bool is_static) {
   int dev = -1;
   e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int lds = 0;
+  e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  p->max_lds_per_block = lds;
   p->d_ws = ws;
   p->bound = true;
   p->device = dev;
@@ -254,7 +294,7 @@ extern "C" int gro_accumulate(gro_plan* p, int32_t b0, int32_t b1, const void* c
     a.fuse_norm = fuse ? 1 : 0;
     a.window = window_size;
     a.acc_nt = acc_nontemporal(p, GRO_MB_ACC_NT) ? 1 : 0;
-    const hipError_t e = launch_accumulate(a, s);
+    const hipError_t e = launch_accumulate(a, micro_lds(p), s);
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
   }
   for (int32_t b = b0; b < b1; ++b) {
@@ -335,7 +375,10 @@ int accumulate_group(gro_plan* p, int32_t b0, int32_t b1, const void* const* d_g
     a.acc = d_acc;
     a.partials = dev_partials(p);
     a.acc_nt = acc_nontemporal(p, GRO_WIN_ACC_NT) ? 1 : 0;
-    const hipError_t e = launch_accumulate_window(a, s);
+    int32_t slots = 1;
+    for (int32_t b = lb; b < le; ++b) slots = std::max(slots, p->bucket_dev[size_t(b)].slots);
+    const int32_t streams = n * slots + (first_micro == 0 ? 0 : 1);
+    const hipError_t e = launch_accumulate_window(a, window_lds(p, streams), s);
     if (e != hipSuccess) return hip_fail(e, "accumulate-window launch");
   }
   for (int32_t b = b0; b < b1; ++b) {

@@ -92,9 +92,15 @@ struct InitLaunch {
   uint16_t* p_bf16;           // may be null
 };
 
-hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s);
+// lds_bytes: dynamic LDS requested per workgroup, which caps the workgroups
+// that share a CU (0: no cap; see wg_cap_lds_bytes).
+hipError_t launch_accumulate(const AccumulateLaunch& a, size_t lds_bytes, hipStream_t s);
 hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s);
-hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s);
+hipError_t launch_accumulate_window(const WindowLaunch& a, size_t lds_bytes, hipStream_t s);
+// Dynamic LDS that leaves room for at most `cap` workgroups of the
+// accumulate passes on one CU (160 KiB of LDS each on gfx950), or 0 when
+// cap <= 0 or the device allows no such allocation per workgroup.
+size_t wg_cap_lds_bytes(int32_t cap, int32_t max_lds_per_block);
 hipError_t launch_norm_partials(const NormLaunch& a, hipStream_t s);
 hipError_t launch_norm_final(const NormFinalLaunch& a, hipStream_t s);
 hipError_t launch_adamw(const AdamWLaunch& a, hipStream_t s);

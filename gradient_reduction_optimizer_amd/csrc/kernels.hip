@@ -988,20 +988,34 @@ hipError_t launch_init_uniform(const InitLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_accumulate(const AccumulateLaunch& a, hipStream_t s) {
+// LDS of one gfx950 CU.  A workgroup that requests a 1/cap share of it
+// (less a margin for the kernels' own 32 bytes and the allocation granule)
+// leaves room for cap workgroups and no more; the kernels do not touch it.
+constexpr int64_t kLdsPerCu = 160 * 1024;
+constexpr int64_t kLdsMargin = 2048;
+
+size_t wg_cap_lds_bytes(int32_t cap, int32_t max_lds_per_block) {
+  if (cap <= 0) return 0;
+  const int64_t b = kLdsPerCu / cap - kLdsMargin;
+  return (b > 0 && b + kLdsMargin / 2 <= max_lds_per_block) ? size_t(b) : 0;
+}
+
+hipError_t launch_accumulate(const AccumulateLaunch& a, size_t lds_bytes, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
   const int64_t blocks = (a.q_end - a.q_begin) + (a.q_begin & 7);
-  if (a.acc_nt) hipLaunchKernelGGL(k_accumulate<true>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
-  else hipLaunchKernelGGL(k_accumulate<false>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  if (a.acc_nt) hipLaunchKernelGGL(k_accumulate<true>, dim3(unsigned(blocks)), dim3(kBlock), lds_bytes, s, a);
+  else hipLaunchKernelGGL(k_accumulate<false>, dim3(unsigned(blocks)), dim3(kBlock), lds_bytes, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_accumulate_window(const WindowLaunch& a, hipStream_t s) {
+hipError_t launch_accumulate_window(const WindowLaunch& a, size_t lds_bytes, hipStream_t s) {
   if (a.q_end <= a.q_begin) return hipSuccess;
   const int64_t blocks = GRO_WIN_MAP == 0 ? (a.q_end - a.q_begin) + (a.q_begin & 7)
                                           : ((a.q_end - a.q_begin + 7) >> 3) * 8;
-  if (a.acc_nt) hipLaunchKernelGGL(k_accumulate_window<true>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
-  else hipLaunchKernelGGL(k_accumulate_window<false>, dim3(unsigned(blocks)), dim3(kBlock), 0, s, a);
+  if (a.acc_nt)
+    hipLaunchKernelGGL(k_accumulate_window<true>, dim3(unsigned(blocks)), dim3(kBlock), lds_bytes, s, a);
+  else
+    hipLaunchKernelGGL(k_accumulate_window<false>, dim3(unsigned(blocks)), dim3(kBlock), lds_bytes, s, a);
   return hipGetLastError();
 }
 

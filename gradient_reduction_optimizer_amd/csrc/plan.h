@@ -91,6 +91,7 @@ struct gro_plan {
   char* d_ws = nullptr;
   bool bound = false;
   int device = -1;
+  int32_t max_lds_per_block = 0;        // the bound device's limit (bytes)
   bool static_ws = false;               // bound to the library's static workspace
   uint64_t static_gen = 0;              // which binding of that workspace is this plan's
 
