@@ -104,19 +104,23 @@ int check_window_acc(const gro_plan* p, int32_t b0, int32_t b1, const float* d_a
 }
 
 // Accumulator store policy of the window pass (GRO_WIN_ACC_NT) and of the
-// per-microbatch pass (GRO_MB_ACC_NT).  The accumulator is read next by the
-// following pass or by AdamW, which walks the chunks in reverse to meet the
-// last-written ones in the 256 MB memory-side Infinity Cache.  That pays
-// while the accumulator is about the cache's size; accumulators several
-// times larger are stored non-temporally (they cannot stay in the cache and
-// would otherwise churn it on their way to HBM), which measured faster.
-// Knobs: 0 never, 1 always, 2 when the accumulator is larger than
+// per-microbatch pass (GRO_MB_ACC_NT), and its load policy in AdamW
+// (GRO_ADAMW_ACC_NT).  The accumulator is read next by the following pass
+// or by AdamW, which walks the chunks in reverse to meet the last-written
+// ones in the 256 MB memory-side Infinity Cache.  That pays while the
+// accumulator is about the cache's size; accumulators several times larger
+// are stored and loaded non-temporally (they cannot stay in the cache and
+// would otherwise churn it on their way to and from HBM), which measured
+// faster.  Knobs: 0 never, 1 always, 2 when the accumulator is larger than
 // GRO_ACC_NT_BYTES.
 #ifndef GRO_WIN_ACC_NT
 #define GRO_WIN_ACC_NT 2
 #endif
 #ifndef GRO_MB_ACC_NT
 #define GRO_MB_ACC_NT 2
+#endif
+#ifndef GRO_ADAMW_ACC_NT
+#define GRO_ADAMW_ACC_NT 2
 #endif
 #ifndef GRO_ACC_NT_BYTES
 #define GRO_ACC_NT_BYTES (512ll << 20)
@@ -573,6 +577,7 @@ extern "C" int gro_clip_adamw(gro_plan* p, const float* d_acc, int32_t window_si
   a.sqrt_bc2 = float(std::sqrt(bc2));
   a.eps = float(hp->eps);
   a.decay = float(1.0 - hp->lr * hp->weight_decay);
+  a.acc_nt = acc_nontemporal(p, GRO_ADAMW_ACC_NT) ? 1 : 0;
   const hipError_t e = launch_adamw(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "clip+AdamW launch");
   reset_window(p);

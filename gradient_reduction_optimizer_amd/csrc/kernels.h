@@ -80,6 +80,7 @@ struct AdamWLaunch {
   int32_t window;
   float beta1, beta2, one_minus_beta1, one_minus_beta2;
   float step_size, sqrt_bc2, eps, decay;
+  int32_t acc_nt;           // 1: load the accumulator with the non-temporal policy
 };
 
 struct InitLaunch {

@@ -801,7 +801,17 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* pb, const f32x4 p) {
   st2u_nt(pb, u32x2{bf16x2_bits(p.x, p.y), bf16x2_bits(p.z, p.w)});
 }
 
+// The accumulator's load: the default policy, so that a step's last
+// accumulate pass's final stretch is met in the Infinity Cache, or (NT) the
+// non-temporal one, for accumulators that pass stored non-temporally.
+template <bool NT>
+__device__ __forceinline__ f32x4 ld4f_acc(const float* p) {
+  if constexpr (NT) return ld4f_nt(p);
+  else return ld4f(p);
+}
+
 // Any chunk: runtime window division, bounds checks, ragged tail.
+template <bool NT>
 __device__ void adamw_generic(const AdamChunk& c, const AdamScalars& k) {
   const int nvec = c.len >> 2;
   for (int v0 = threadIdx.x; v0 < nvec; v0 += kUnroll * kBlock) {
@@ -810,7 +820,7 @@ __device__ void adamw_generic(const AdamChunk& c, const AdamScalars& k) {
     for (int u = 0; u < kUnroll; ++u) {
       const int v = v0 + u * kBlock;
       if (v < nvec) {
-        a[u] = ld4f(c.acc + 4 * v);
+        a[u] = ld4f_acc<NT>(c.acc + 4 * v);
         p[u] = ld4f_nt(c.p + 4 * v);
         m[u] = ld4f_nt(c.m + 4 * v);
         w[u] = ld4f_nt(c.v + 4 * v);
@@ -842,7 +852,7 @@ __device__ void adamw_generic(const AdamChunk& c, const AdamScalars& k) {
 
 // A full chunk with the window division (WM) and the BF16 copy fixed at
 // compile time: no bounds checks, no per-element branches.
-template <int WM, bool BF16>
+template <int WM, bool BF16, bool NT>
 __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
   constexpr int nvec = kChunkElems / 4;
 #pragma unroll 1
@@ -851,7 +861,7 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
 #pragma unroll
     for (int u = 0; u < kUnrollAdam; ++u) {
       const int v = v0 + u * kBlock;
-      a[u] = ld4f(c.acc + 4 * v);
+      a[u] = ld4f_acc<NT>(c.acc + 4 * v);
       p[u] = ld4f_nt(c.p + 4 * v);
       m[u] = ld4f_nt(c.m + 4 * v);
       w[u] = ld4f_nt(c.v + 4 * v);
@@ -874,6 +884,7 @@ __device__ void adamw_full(const AdamChunk& c, const AdamScalars& k) {
 #ifndef GRO_ADAMW_FORWARD
 #define GRO_ADAMW_FORWARD 0
 #endif
+template <bool NT>
 __global__ __launch_bounds__(kBlock, GRO_ADAMW_MIN_BLOCKS) void k_adamw(const AdamWLaunch P) {
   const int64_t q = GRO_ADAMW_FORWARD ? int64_t(blockIdx.x) : P.n_chunks - 1 - int64_t(blockIdx.x);
   if (q >= P.n_chunks) return;
@@ -906,14 +917,14 @@ __global__ __launch_bounds__(kBlock, GRO_ADAMW_MIN_BLOCKS) void k_adamw(const Ad
   if (c.len == kChunkElems) {
     const int wm = div_mode(k.wdiv);
     if (wm == kMulInv) {
-      if (c.pb) adamw_full<kMulInv, true>(c, k);
-      else adamw_full<kMulInv, false>(c, k);
+      if (c.pb) adamw_full<kMulInv, true, NT>(c, k);
+      else adamw_full<kMulInv, false, NT>(c, k);
     } else {
-      if (c.pb) adamw_full<kIeeeDiv, true>(c, k);
-      else adamw_full<kIeeeDiv, false>(c, k);
+      if (c.pb) adamw_full<kIeeeDiv, true, NT>(c, k);
+      else adamw_full<kIeeeDiv, false, NT>(c, k);
     }
   } else {
-    adamw_generic(c, k);
+    adamw_generic<NT>(c, k);
   }
 }
 
@@ -1034,7 +1045,8 @@ hipError_t launch_norm_final(const NormFinalLaunch& a, hipStream_t s) {
 
 hipError_t launch_adamw(const AdamWLaunch& a, hipStream_t s) {
   if (a.n_chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_adamw, dim3(unsigned(a.n_chunks)), dim3(kBlock), 0, s, a);
+  if (a.acc_nt) hipLaunchKernelGGL(k_adamw<true>, dim3(unsigned(a.n_chunks)), dim3(kBlock), 0, s, a);
+  else hipLaunchKernelGGL(k_adamw<false>, dim3(unsigned(a.n_chunks)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
