@@ -155,9 +155,11 @@ def pattern_probes(st, n_micro: int, c_mix: int, N: int, flush, stream, log, rep
     shapes = {"k_adamw": (0, 0, 30), "k_accumulate": (2, 1, 10)}
     if probe_k:
         shapes["k_accumulate_window"] = (1, k, 2 * k + 4)
-    res = {"note": "same arrays, element types, cache policy and chunking as the kernel, trivial arithmetic, "
-                   "random data; k_accumulate is its later-microbatch shape (BF16 in, FP32 read and written); "
-                   "'wide': the same bytes with 8 elements per lane access instead of the kernels' 4",
+    res = {"note": "same arrays, element types and chunking as the kernel, trivial arithmetic, random data; "
+                   "the cache policy the kernels use on accumulators up to 512 MiB (the accumulator default, "
+                   "every other stream non-temporal) and no workgroup cap, on every plan; k_accumulate is its "
+                   "later-microbatch shape (BF16 in, FP32 read and written); 'wide': the same bytes with 8 "
+                   "elements per lane access instead of the kernels' 4",
            "elements": n, "window_streams": probe_k}
     for name, (pattern, kk, b) in shapes.items():
         res[name] = {"GBps": run(pattern, kk, b, False)}
