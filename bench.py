@@ -772,10 +772,21 @@ def main():
         del t
         flush_buf = None
         torch.cuda.empty_cache()
-        out["dense_1b_shard"] = dense_1b_child(args, log)
+        out["dense_1b_shard"] = _child_or_error(dense_1b_child, args, log)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_child(args, log)
+        out["cpu_baseline"] = _child_or_error(cpu_baseline_child, args, log)
     print(json.dumps(out), flush=True)
+
+
+def _child_or_error(fn, args, log):
+    """A secondary entry measured in a child process; if that process fails,
+    the line still carries the headline, with the failure stated in place of
+    the entry."""
+    try:
+        return fn(args, log)
+    except (RuntimeError, ValueError, OSError) as e:  # json.JSONDecodeError is a ValueError
+        log(f"{fn.__name__}: {e}")
+        return {"error": str(e)}
 
 
 def cpu_baseline_child(args, log) -> dict:
