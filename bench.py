@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of the workload's elements the oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the headline step")
     ap.add_argument("--only-cpu-baseline", action="store_true",
                     help="print only the CPU oracle's timing as one JSON line, without touching the GPU "
                          "(bench.py runs itself this way in a child process)")
@@ -577,6 +578,38 @@ class StepTimer:
                              "frac": step_bytes / (ms * 1e6) / HBM_PEAK_GBS},
                 "final_norm": norm}
 
+    def time_graph(self, mode: str, n: int) -> dict:
+        """The same step captured once in a HIP graph on a side stream and
+        replayed: `warmup` untimed replays, then `steps` replays timed by the
+        wall clock between two device synchronisations.  The captured step
+        keeps its step count (a kernel argument); the work per replay is the
+        eager step's."""
+        torch, args = self.torch, self.args
+        side = torch.cuda.Stream()
+        side.wait_stream(self.stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        keep = (self.s, self.stream)
+        try:
+            with torch.cuda.graph(g, stream=side):
+                self.s, self.stream = side.cuda_stream, side
+                self.one_step(mode, n, None)
+        finally:
+            self.s, self.stream = keep
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        norm, _, finite = self.B.gro_plan_get_norm(self.plan.handle)
+        if not finite:
+            raise RuntimeError("the graph replays' norm is not finite")
+        del g
+        return {"ms_per_step": ms, "value": self.N / (ms * 1e-3) / 1e9, "final_norm": norm}
+
     def time_cold(self, mode: str, n: int) -> dict:
         """The same steps with the cache flushed before every call: the sum
         of the calls' event durations, without launch gaps."""
@@ -691,6 +724,7 @@ def main():
     mb = t.time_mode("microbatch", n)
     grp = t.time_mode("group", n, groups) if not args.no_group else None
     wnd = t.time_mode("window", n)
+    grf = None if args.no_graph else t.time_graph("window", n)
     dom = wnd["dominant"]
     achieved = wnd["kernels"][dom]["GBps"]
     out = {
@@ -737,6 +771,11 @@ def main():
             "step_hbm": grp["step_hbm"], "kernels": grp["kernels"]},
         "context": {"pages_ms_per_update_67M": [3.255, 2.624], "hardware_of_pages": "not stated"},
     }
+    if grf is not None:
+        out["graph_replay"] = {
+            "note": "the headline step (window call, norm, clip + AdamW: three launches) captured once in a "
+                    "HIP graph and replayed, against the same step issued eagerly",
+            "ms_per_step": grf["ms_per_step"], "value": grf["value"], "eager_ms_per_step": wnd["ms_per_step"]}
     if flush_buf is not None:
         out["cold_cache"] = {
             "protocol": f"an untimed {args.flush_mib} MiB read of an unrelated buffer before every call; "
