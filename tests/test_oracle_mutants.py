@@ -187,6 +187,39 @@ def _v_unclipped(g, coef, p, m, v, sc, decayed):
     return p, m, v, M.f32_to_bf16(p)
 
 
+def _m_unclipped(g, coef, p, m, v, sc, decayed):
+    gh = g * F32(coef)
+    p = p * (sc.decay if decayed else F32(1.0))
+    m = sc.beta1 * m + sc.one_minus_beta1 * g
+    v = sc.beta2 * v + sc.one_minus_beta2 * (gh * gh)
+    d = np.sqrt(v) / sc.sqrt_bc2 + sc.eps
+    p = p - sc.step_size * (m / d)
+    return p, m, v, M.f32_to_bf16(p)
+
+
+def _philox_key_fixed(counter, key):
+    c = [int(x) for x in counter]
+    k = [int(x) for x in key]
+    MASK = (1 << 64) - 1
+    for _ in range(10):
+        p0 = 0xD2E7470EE14C6C93 * c[0]
+        p1 = 0xCA5A826395121157 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k[0], p1 & MASK, (p0 >> 64) ^ c[3] ^ k[1], p0 & MASK]
+    return c
+
+
+def _philox_multipliers_swapped(counter, key):
+    c = [int(x) for x in counter]
+    k = [int(x) for x in key]
+    MASK = (1 << 64) - 1
+    for _ in range(10):
+        p0 = 0xCA5A826395121157 * c[0]
+        p1 = 0xD2E7470EE14C6C93 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k[0], p1 & MASK, (p0 >> 64) ^ c[3] ^ k[1], p0 & MASK]
+        k = [(k[0] + 0x9E3779B97F4A7C15) & MASK, (k[1] + 0xBB67AE8584CAA73B) & MASK]
+    return c
+
+
 def _eps_before_bias_correction(g, coef, p, m, v, sc, decayed):
     gh = g * F32(coef)
     p = p * (sc.decay if decayed else F32(1.0))
@@ -297,6 +330,9 @@ MUTANTS = {
     "init_wrong_word": ("init_uniform", _init_wrong_word),
     "init_low_bits": ("init_uniform", _init_low_bits),
     "init_one_sided": ("init_uniform", _init_one_sided),
+    "m_from_unclipped_gradient": ("adamw_update", _m_unclipped),
+    "philox_key_not_bumped": ("philox4x64_10", _philox_key_fixed),
+    "philox_multipliers_swapped": ("philox4x64_10", _philox_multipliers_swapped),
 }
 
 
