@@ -43,7 +43,11 @@
  *    work.  Non-finite data is reported through gro_plan_get_norm's `finite`
  *    flag, not a return code, because device work is asynchronous.
  *  - Only gro_plan_bind, gro_plan_bind_static, gro_init_uniform and
- *    gro_plan_get_norm wait for the device.
+ *    gro_plan_get_norm wait for the device.  The step's calls
+ *    (gro_accumulate*, gro_reduce_norm, gro_clip_adamw) only enqueue kernels
+ *    -- no allocation, no synchronization, no memory fill -- so a step may be
+ *    captured in a HIP graph after binding and replayed; the replay repeats
+ *    the captured arguments, the AdamW step count included.
  *  - Not thread-safe per plan; distinct plans may be used from distinct
  *    threads.
  */
