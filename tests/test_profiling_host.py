@@ -97,6 +97,18 @@ def test_bench_times_the_cpu_oracle_without_the_gpu():
     assert out["one_core"]["cores"] == 1 and out["value"] > 0
 
 
+def test_a_failed_child_entry_is_reported_in_the_line():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    def fails(args, log):
+        raise RuntimeError("the child's process failed with exit code 134")
+
+    got = bench._child_or_error(fails, None, lambda *a: None)
+    assert got == {"error": "the child's process failed with exit code 134"}
+    assert bench._child_or_error(lambda args, log: {"value": 1.0}, None, lambda *a: None) == {"value": 1.0}
+
+
 def test_exact_sum_of_squares_matches_a_correctly_rounded_sum():
     """bench.py's all-cores oracle timing adds the workers' norm partials
     exactly; rounded once, that must equal math.fsum of the squares (the
