@@ -120,7 +120,7 @@ def pattern_probes(st, n_micro: int, c_mix: int, N: int, flush, stream, log, rep
         return None
     lib = ctypes.CDLL(PROBE_LIB)
     V = ctypes.c_void_p
-    lib.gro_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int64, V, V, V, V, V, V, ctypes.c_int, V]
+    lib.gro_probe_stream.argtypes = [ctypes.c_int, ctypes.c_int64, V, V, V, V, V, V, ctypes.c_int, ctypes.c_int, V]
     lib.gro_probe_stream.restype = ctypes.c_int
     n = (int(st.acc.numel()) // 4096) * 4096
     k = int(round(n_micro * c_mix / N))  # BF16 streams the window kernel reads per element
@@ -134,6 +134,15 @@ def pattern_probes(st, n_micro: int, c_mix: int, N: int, flush, stream, log, rep
     gp = (V * len(g))(*[x.data_ptr() for x in g])
     s = stream.cuda_stream
     ptrs = [st.acc.data_ptr(), st.master.data_ptr(), st.m.data_ptr(), st.v.data_ptr(), st.p_bf16.data_ptr()]
+    # The launch policy the library takes for a plan of this size (the rule in
+    # csrc/abi.hip, acc_nontemporal, window_lds and micro_lds), so that each
+    # probe runs as its kernel does: above 512 MiB of accumulator, that stream
+    # moves non-temporally, and the accumulate passes run at most 2 (window
+    # pass of 12 or more streams) or 3 (5 to 11 streams; per-microbatch pass)
+    # workgroups per CU.
+    large = int(st.acc.numel()) * 4 > (512 << 20)
+    win_cap = (2 if k >= 12 else 3 if k >= 5 else 0) if large else 0
+    flags = {0: int(large), 1: int(large) | (win_cap << 8), 2: int(large) | ((3 if large else 0) << 8)}
 
     def run(pattern, kk, nbytes, cold):
         ev = []
@@ -143,7 +152,7 @@ def pattern_probes(st, n_micro: int, c_mix: int, N: int, flush, stream, log, rep
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            rc = lib.gro_probe_stream(pattern, n, *ptrs, gp, kk, s)
+            rc = lib.gro_probe_stream(pattern, n, *ptrs, gp, kk, flags.get(pattern % 3, 0) if pattern < 6 else 0, s)
             e1.record(stream)
             if rc != 0:
                 raise RuntimeError(f"gro_probe_stream({pattern}) returned {rc}")
@@ -156,12 +165,13 @@ def pattern_probes(st, n_micro: int, c_mix: int, N: int, flush, stream, log, rep
     shapes = {"k_adamw": (0, 0, 30), "k_accumulate": (2, 1, 10)}
     if probe_k:
         shapes["k_accumulate_window"] = (1, k, 2 * k + 4)
-    res = {"note": "same arrays, element types and chunking as the kernel, trivial arithmetic, random data; "
-                   "the cache policy the kernels use on accumulators up to 512 MiB (the accumulator default, "
-                   "every other stream non-temporal) and no workgroup cap, on every plan; k_accumulate is its "
-                   "later-microbatch shape (BF16 in, FP32 read and written); 'wide': the same bytes with 8 "
-                   "elements per lane access instead of the kernels' 4",
-           "elements": n, "window_streams": probe_k}
+    res = {"note": "same arrays, element types, chunking, cache policy and workgroups per CU as the kernel "
+                   "on a plan of this size, trivial arithmetic, random data; k_accumulate is its later-microbatch "
+                   "shape (BF16 in, FP32 read and written); 'wide': the same bytes with 8 elements per lane "
+                   "access instead of the kernels' 4",
+           "elements": n, "window_streams": probe_k,
+           "launch": {"accumulator_nontemporal": large, "window_wg_per_cu": win_cap or None,
+                      "accumulate_wg_per_cu": 3 if large else None}}
     for name, (pattern, kk, b) in shapes.items():
         res[name] = {"GBps": run(pattern, kk, b, False)}
         if flush is not None:
@@ -679,10 +689,18 @@ def dense_1b_entry(args, log, flush_buf) -> dict:
                                             "microbatch_call": t.time_cold("microbatch", full)}
     if not args.no_probe:
         try:
-            out["pattern_probe"] = pattern_probes(t.st, full, t.c_mix, t.N,
-                                                  t.flush if flush_buf is not None else None, t.stream, log)
+            att = pattern_probes(t.st, full, t.c_mix, t.N, t.flush if flush_buf is not None else None,
+                                 t.stream, log)
         except (OSError, RuntimeError) as e:
             log(f"pattern probes not run: {e}")
+            att = None
+        out["pattern_probe"] = att
+        # The window and AdamW probes move exactly these kernels' bytes (the
+        # accumulate probe reads one slot, this plan's kernel two).
+        for kd in ((out["full_window"]["window_call"]["kernels"],) if att else ()):
+            for name in ("k_accumulate_window", "k_adamw"):
+                if name in kd and name in att:
+                    kd[name]["frac_of_pattern_probe"] = kd[name]["GBps"] / att[name]["GBps"]
     return out
 
 

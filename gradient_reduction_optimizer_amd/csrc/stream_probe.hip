@@ -10,16 +10,19 @@
 // width comparison weighs.  Measurement infrastructure only (built into
 // libgro_probe.so, used by bench.py); not part of the gro_* ABI.
 //
-//   pattern 0 / 3, AdamW:       read acc (default policy) and p, m, v
+//   pattern 0 / 3, AdamW:       read acc (default policy; flags bit 0:
+//                               non-temporal) and p, m, v
 //                               (non-temporal); write p, m, v and a BF16 copy
 //                               (non-temporal).  30 bytes per element; chunks
 //                               in reverse order; 16 elements per lane.
 //   pattern 1 / 4, window:      read k BF16 streams (non-temporal); write one
-//                               FP32 stream (default policy).  2k + 4 bytes
+//                               FP32 stream (default policy; flags bit 0:
+//                               non-temporal).  2k + 4 bytes
 //                               per element; 8 elements per lane in flight
 //                               per stream.
 //   pattern 2 / 5, accumulate:  read one BF16 stream (non-temporal) and the
-//                               FP32 stream; write the FP32 stream.  10 bytes
+//                               FP32 stream; write the FP32 stream (flags
+//                               bit 0: non-temporally).  10 bytes
 //                               per element; 8 elements per lane in flight.
 // Patterns 0-2 use 4 elements per lane access, 3-5 use 8.
 //
@@ -36,7 +39,13 @@
 // Arguments: n elements (a multiple of 4,096); device pointers as the pattern
 // needs them (unused ones may be NULL); for the window patterns `k` BF16
 // stream pointers in `g`, k in 1..8, 12 or 16 (the window kernel reads window
-// length x slots streams).  Returns 0, -1 for bad arguments, or a hipError_t.
+// length x slots streams); `flags` the launch policy the kernels take on
+// large accumulators: bit 0 moves the accumulator's stream (acc read by the
+// AdamW pattern, the FP32 stream written by the window and accumulate
+// patterns) with the non-temporal policy, bits 8-15 (0-16) cap the
+// workgroups sharing a CU as the kernels do, with dynamic LDS that the probe
+// does not use (0: no cap).  Returns 0, -1 for bad arguments, or a
+// hipError_t.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -79,6 +88,17 @@ __device__ __forceinline__ f32x4 load_nt(const float* p) {
 __device__ __forceinline__ void store_nt(float* p, f32x4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
 }
+// The accumulator's stream: default policy, or non-temporal (NT).
+template <bool NT>
+__device__ __forceinline__ f32x4 load_acc(const float* p) {
+  if constexpr (NT) return load_nt(p);
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void store_acc(float* p, f32x4 x) {
+  if constexpr (NT) store_nt(p, x);
+  else *reinterpret_cast<f32x4*>(p) = x;
+}
 
 struct Streams {
   const float* acc;
@@ -92,7 +112,7 @@ struct Streams {
 
 // Lane accesses of W elements; U of them per lane and stream in flight.  A
 // lane's access u covers elements base + W * (v0 + u * kLanes) .. + W - 1.
-template <int W>
+template <int W, bool NT>
 __global__ __launch_bounds__(kLanes) void probe_adamw(const Streams s, int64_t n_chunks) {
   constexpr int U = 16 / W, H = W / 4;
   const int64_t base = (n_chunks - 1 - int64_t(blockIdx.x)) * kChunk;
@@ -102,7 +122,7 @@ __global__ __launch_bounds__(kLanes) void probe_adamw(const Streams s, int64_t n
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       const int64_t e = base + W * (threadIdx.x + u * kLanes) + 4 * h;
-      a[u][h] = *reinterpret_cast<const f32x4*>(s.acc + e);
+      a[u][h] = load_acc<NT>(s.acc + e);
       p[u][h] = load_nt(s.p + e);
       m[u][h] = load_nt(s.m + e);
       v[u][h] = load_nt(s.v + e);
@@ -128,7 +148,7 @@ __global__ __launch_bounds__(kLanes) void probe_adamw(const Streams s, int64_t n
   }
 }
 
-template <int K, int W>
+template <int K, int W, bool NT>
 __global__ __launch_bounds__(kLanes) void probe_window(const Streams s) {
   constexpr int U = 8 / W, H = W / 4;
   const int64_t base = int64_t(blockIdx.x) * kChunk;
@@ -149,13 +169,12 @@ __global__ __launch_bounds__(kLanes) void probe_window(const Streams s) {
         for (int h = 0; h < H; ++h) t[h] = t[h] + x[h];
       }
 #pragma unroll
-      for (int h = 0; h < H; ++h)
-        *reinterpret_cast<f32x4*>(s.p + base + W * (v0 + u * kLanes) + 4 * h) = t[h];
+      for (int h = 0; h < H; ++h) store_acc<NT>(s.p + base + W * (v0 + u * kLanes) + 4 * h, t[h]);
     }
   }
 }
 
-template <int W>
+template <int W, bool NT>
 __global__ __launch_bounds__(kLanes) void probe_accumulate(const Streams s) {
   constexpr int U = 8 / W, H = W / 4;
   const int64_t base = int64_t(blockIdx.x) * kChunk;
@@ -174,8 +193,7 @@ __global__ __launch_bounds__(kLanes) void probe_accumulate(const Streams s) {
       f32x4 t[H];
       widen_all(r[u], t);
 #pragma unroll
-      for (int h = 0; h < H; ++h)
-        *reinterpret_cast<f32x4*>(s.p + base + W * (v0 + u * kLanes) + 4 * h) = old[u][h] + t[h];
+      for (int h = 0; h < H; ++h) store_acc<NT>(s.p + base + W * (v0 + u * kLanes) + 4 * h, old[u][h] + t[h]);
     }
   }
 }
@@ -210,29 +228,43 @@ __global__ __launch_bounds__(kLanes) void probe_copy(const Streams s) {
   for (int u = 0; u < 4; ++u) *reinterpret_cast<f32x4*>(s.p + base + 4 * (threadIdx.x + u * kLanes)) = x[u];
 }
 
-template <int W>
-hipError_t launch_window(int k, const dim3 grid, const Streams& s, hipStream_t st) {
+template <int W, bool NT>
+hipError_t launch_window(int k, const dim3 grid, size_t lds, const Streams& s, hipStream_t st) {
   const dim3 block(kLanes);
   switch (k) {
-    case 1: hipLaunchKernelGGL((probe_window<1, W>), grid, block, 0, st, s); break;
-    case 2: hipLaunchKernelGGL((probe_window<2, W>), grid, block, 0, st, s); break;
-    case 3: hipLaunchKernelGGL((probe_window<3, W>), grid, block, 0, st, s); break;
-    case 4: hipLaunchKernelGGL((probe_window<4, W>), grid, block, 0, st, s); break;
-    case 5: hipLaunchKernelGGL((probe_window<5, W>), grid, block, 0, st, s); break;
-    case 6: hipLaunchKernelGGL((probe_window<6, W>), grid, block, 0, st, s); break;
-    case 7: hipLaunchKernelGGL((probe_window<7, W>), grid, block, 0, st, s); break;
-    case 8: hipLaunchKernelGGL((probe_window<8, W>), grid, block, 0, st, s); break;
-    case 12: hipLaunchKernelGGL((probe_window<12, W>), grid, block, 0, st, s); break;
-    case 16: hipLaunchKernelGGL((probe_window<16, W>), grid, block, 0, st, s); break;
+    case 1: hipLaunchKernelGGL((probe_window<1, W, NT>), grid, block, lds, st, s); break;
+    case 2: hipLaunchKernelGGL((probe_window<2, W, NT>), grid, block, lds, st, s); break;
+    case 3: hipLaunchKernelGGL((probe_window<3, W, NT>), grid, block, lds, st, s); break;
+    case 4: hipLaunchKernelGGL((probe_window<4, W, NT>), grid, block, lds, st, s); break;
+    case 5: hipLaunchKernelGGL((probe_window<5, W, NT>), grid, block, lds, st, s); break;
+    case 6: hipLaunchKernelGGL((probe_window<6, W, NT>), grid, block, lds, st, s); break;
+    case 7: hipLaunchKernelGGL((probe_window<7, W, NT>), grid, block, lds, st, s); break;
+    case 8: hipLaunchKernelGGL((probe_window<8, W, NT>), grid, block, lds, st, s); break;
+    case 12: hipLaunchKernelGGL((probe_window<12, W, NT>), grid, block, lds, st, s); break;
+    case 16: hipLaunchKernelGGL((probe_window<16, W, NT>), grid, block, lds, st, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipSuccess;
 }
 
+template <int W, bool NT>
+void launch_adamw(const dim3 grid, size_t lds, const Streams& s, int64_t chunks, hipStream_t st) {
+  hipLaunchKernelGGL((probe_adamw<W, NT>), grid, dim3(kLanes), lds, st, s, chunks);
+}
+
+template <int W, bool NT>
+void launch_accumulate(const dim3 grid, size_t lds, const Streams& s, hipStream_t st) {
+  hipLaunchKernelGGL((probe_accumulate<W, NT>), grid, dim3(kLanes), lds, st, s);
+}
+
+// Dynamic LDS that leaves room for at most `cap` workgroups on one gfx950
+// CU (160 KiB of LDS), as the library's launches request it; 0: no cap.
+size_t cap_lds(int cap) { return cap > 0 ? size_t(160 * 1024 / cap - 2048) : 0; }
+
 }  // namespace
 
 extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float* p, float* m, float* v,
-                                uint16_t* pb, const uint16_t* const* g, int k, void* stream) {
+                                uint16_t* pb, const uint16_t* const* g, int k, int flags, void* stream) {
   if (n <= 0 || n % kChunk != 0) return -1;
   const int64_t chunks = n / kChunk;
   if (chunks > 0x7fffffff) return -1;
@@ -243,6 +275,11 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
   s.v = v;
   s.pb = pb;
   s.k = k;
+  if (flags & ~0xff01) return -1;
+  const int cap = (flags >> 8) & 0xff;
+  if (cap > 16) return -1;
+  const bool nt = (flags & 1) != 0;
+  const size_t lds = cap_lds(cap);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(chunks)), block(kLanes);
   const bool wide = pattern >= 3;
@@ -250,8 +287,8 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
     case 0:
     case 3:
       if (!acc || !p || !m || !v || !pb) return -1;
-      if (wide) hipLaunchKernelGGL(probe_adamw<8>, grid, block, 0, st, s, chunks);
-      else hipLaunchKernelGGL(probe_adamw<4>, grid, block, 0, st, s, chunks);
+      if (wide) nt ? launch_adamw<8, true>(grid, lds, s, chunks, st) : launch_adamw<8, false>(grid, lds, s, chunks, st);
+      else nt ? launch_adamw<4, true>(grid, lds, s, chunks, st) : launch_adamw<4, false>(grid, lds, s, chunks, st);
       break;
     case 1:
     case 4: {
@@ -261,7 +298,10 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
         if (!g[j]) return -1;
         s.g[j] = g[j];
       }
-      const hipError_t e = wide ? launch_window<8>(k, grid, s, st) : launch_window<4>(k, grid, s, st);
+      const hipError_t e = wide ? (nt ? launch_window<8, true>(k, grid, lds, s, st)
+                                      : launch_window<8, false>(k, grid, lds, s, st))
+                                : (nt ? launch_window<4, true>(k, grid, lds, s, st)
+                                      : launch_window<4, false>(k, grid, lds, s, st));
       if (e != hipSuccess) return -1;
       break;
     }
@@ -269,20 +309,20 @@ extern "C" int gro_probe_stream(int pattern, int64_t n, const float* acc, float*
     case 5:
       if (!p || !g || !g[0]) return -1;
       s.g[0] = g[0];
-      if (wide) hipLaunchKernelGGL(probe_accumulate<8>, grid, block, 0, st, s);
-      else hipLaunchKernelGGL(probe_accumulate<4>, grid, block, 0, st, s);
+      if (wide) nt ? launch_accumulate<8, true>(grid, lds, s, st) : launch_accumulate<8, false>(grid, lds, s, st);
+      else nt ? launch_accumulate<4, true>(grid, lds, s, st) : launch_accumulate<4, false>(grid, lds, s, st);
       break;
     case 6:
       if (!p || !m) return -1;
-      hipLaunchKernelGGL(probe_read, grid, block, 0, st, s);
+      hipLaunchKernelGGL(probe_read, grid, block, lds, st, s);
       break;
     case 7:
       if (!p) return -1;
-      hipLaunchKernelGGL(probe_write, grid, block, 0, st, s);
+      hipLaunchKernelGGL(probe_write, grid, block, lds, st, s);
       break;
     case 8:
       if (!acc || !p) return -1;
-      hipLaunchKernelGGL(probe_copy, grid, block, 0, st, s);
+      hipLaunchKernelGGL(probe_copy, grid, block, lds, st, s);
       break;
     default:
       return -1;
